@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = the three NVFP4 projections of an H3 block at the
+canonical 37,810-token shape, each producer + GEMM on one stream:
+
+  QKV  modulation producer (x [37810,5376], 2 segments) -> GEMM N=21504, K=5376
+  FC1  modulation producer (same x, own shift/scale)    -> GEMM N=14336, K=5376
+  FC2  SwiGLU producer (gate/up [37810, 2*14336])       -> GEMM N=5376,  K=14336
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts;
+weights are prepacked to NVFP4 (untimed).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "producer GB/s (% HBM peak) + NVFP4 GEMM TFLOP/s at M=37810 QKV/FC1/FC2"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    return p.parse_args()
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "nvfp4_activation_quantization_segment_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(kernel: str, source_hash: str):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain-copy calibration), if they were taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        e = data.get(kernel)
+        if not e or e.get("source_hash") != source_hash:
+            return None
+        return float(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the producer shards by rows with one 4-byte max all-reduce, which this build does not run)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_activation_quantization_segment_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_setup = time.time()
+    wq, wf1, wf2 = synth.workload("qkv"), synth.workload("fc1"), synth.workload("fc2")
+    M = wq.M
+    M_pad = wq.m_pad
+    x_h = wq.x()
+    x = up(x_h)
+    segs = {}
+    for w in (wq, wf1):
+        rs, sh, sc = w.segments()
+        segs[w.name] = (rs, up(sh), up(sc))
+    gu_h = wf2.gate_up()
+    gu = up(gu_h)
+    weights = {}
+    for w in (wq, wf1, wf2):
+        wt = up(w.weight())
+        with torch.cuda.stream(stream):
+            weights[w.name] = nv.quantize_weight(wt, stream=stream)
+        stream.synchronize()
+        del wt
+    # outputs and per-projection scratch, allocated once
+    bufs = {}
+    for w in (wq, wf1, wf2):
+        K = w.K
+        bufs[w.name] = dict(
+            q=torch.empty((M_pad, K // 2), dtype=torch.uint8, device=dev),
+            s=torch.empty((M_pad, K // 16), dtype=torch.uint8, device=dev),
+            ts=torch.empty(1, dtype=torch.float32, device=dev),
+            amax=torch.empty(1, dtype=torch.float32, device=dev),
+            out=torch.empty((M, w.N), dtype=torch.bfloat16, device=dev),
+            ws=torch.zeros(int(nv.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev),
+        )
+    seg_structs = {n: nv.make_segments(*segs[n]) for n in segs}
+    F = wf2.K
+    gate_ptr, up_ptr = gu.data_ptr(), gu.data_ptr() + 2 * F
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    # kernel sequence of one step: (label, kind, fn)
+    def launches():
+        seq = []
+        for w in (wq, wf1):
+            b = bufs[w.name]
+            seg = seg_structs[w.name][0]
+            qw, sfw, tw = weights[w.name]
+            seq.append((f"{w.name}.absmax", "mod_absmax",
+                        lambda b=b, seg=seg, w=w: nv.nvfp4_modulate_absmax(x, M, w.K, w.K, seg, b["ws"], b["ts"],
+                                                                           b["amax"], stream)))
+            seq.append((f"{w.name}.pack", "mod_pack",
+                        lambda b=b, seg=seg, w=w: nv.nvfp4_modulate_pack(x, M, w.K, w.K, seg, b["ts"], b["q"],
+                                                                         b["s"], M_pad, stream)))
+            seq.append((f"{w.name}.gemm", "gemm",
+                        lambda b=b, w=w, qw=qw, sfw=sfw, tw=tw: nv.nvfp4_gemm(
+                            b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, w.N, w.K, b["out"], w.N, stream)))
+        b = bufs["fc2"]
+        qw, sfw, tw = weights["fc2"]
+        seq.append(("fc2.absmax", "swiglu_absmax",
+                    lambda: nv.nvfp4_swiglu_absmax(gate_ptr, up_ptr, M, F, 2 * F, b["ws"], b["ts"], b["amax"],
+                                                   stream)))
+        seq.append(("fc2.pack", "swiglu_pack",
+                    lambda: nv.nvfp4_swiglu_pack(gate_ptr, up_ptr, M, F, 2 * F, b["ts"], b["q"], b["s"], M_pad,
+                                                 stream)))
+        seq.append(("fc2.gemm", "gemm",
+                    lambda: nv.nvfp4_gemm(b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, wf2.N, wf2.K, b["out"],
+                                          wf2.N, stream)))
+        return seq
+
+    seq = launches()
+    n = len(seq)
+
+    def run_step(events=None):
+        for i, (_, _, fn) in enumerate(seq):
+            if events is not None:
+                events[i].record(stream)
+            fn()
+        if events is not None:
+            events[n].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    stream.synchronize()
+
+    # timed region: K steps, events between launches on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        run_step(evs[k])
+    end.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per = {label: [] for label, _, _ in seq}
+    for k in range(args.steps):
+        for i, (label, _, _) in enumerate(seq):
+            per[label].append(evs[k][i].elapsed_time(evs[k][i + 1]))
+    med = {label: float(np.median(v)) for label, v in per.items()}
+
+    # algorithmic work
+    def mod_bytes(K):  # two reads of x + QDATA + SFA written (padded rows included)
+        return 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
+
+    def swiglu_bytes(F):  # two reads of gate+up + QDATA + SFA
+        return 2 * M * 2 * F * 2 + M_pad * (F // 2 + F // 16)
+
+    flops = {w.name: 2.0 * M * w.N * w.K for w in (wq, wf1, wf2)}
+    prod_bytes = {"qkv": mod_bytes(wq.K), "fc1": mod_bytes(wf1.K), "fc2": swiglu_bytes(F)}
+    total_flops = sum(flops.values())
+    gemm_ms = {nme: med[f"{nme}.gemm"] for nme in flops}
+    prod_ms = {nme: med[f"{nme}.absmax"] + med[f"{nme}.pack"] for nme in flops}
+    gemm_avg_ms = float(np.mean([np.mean(per[f"{nme}.gemm"]) for nme in flops]))
+    gemm_achieved = (total_flops / 3) / (gemm_avg_ms * 1e-3) / 1e12
+
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+    gemm_hash = src_hash("gemm.hip", "nvfp4_device.h")
+    traffic = traffic_entry("gemm_kernel", gemm_hash)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 e2m1/e4m3 operands, f16 MFMA, fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded; shapes of the H3 block at 37,810 tokens)",
+        "config": {
+            "workload": "H3 block NVFP4 projections QKV+FC1+FC2, M=37810 (padded 37824): modulation producer "
+                        "K=5376 -> GEMM N=21504 and N=14336; SwiGLU producer F=14336 -> GEMM N=5376",
+            "M": M, "M_pad": M_pad,
+            "value_definition": "total GEMM flop of the three projections / whole step time (producers included)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_kernel (3 launches per step: QKV, FC1, FC2)",
+            "achieved": round(gemm_achieved, 1),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_achieved / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(gemm_avg_ms, 4),
+            "flop_per_launch_avg": total_flops / 3,
+        },
+        "producer": {
+            nme: {"ms": round(prod_ms[nme], 4), "absmax_ms": round(med[f"{nme}.absmax"], 4),
+                  "pack_ms": round(med[f"{nme}.pack"], 4), "bytes": prod_bytes[nme],
+                  "GBps": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            for nme in flops
+        },
+        "gemm": {
+            nme: {"ms": round(gemm_ms[nme], 4), "flop": flops[nme],
+                  "TFLOPs": round(flops[nme] / (gemm_ms[nme] * 1e-3) / 1e12, 1),
+                  "frac_peak": round(flops[nme] / (gemm_ms[nme] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+            for nme in flops
+        },
+        "timing": {"wall_ms_timed_region": round(wall_ms, 2), "event_ms_timed_region": round(total_ms, 2),
+                   "setup_s": round(setup_s, 1), "kernel_source_hash": gemm_hash},
+        "context": "pages' numbers (GB10/DGX Spark): fused producer 6.02 ms for the block-24 QKV input vs "
+                   "10.47/10.60 ms unfused modulation; CUTLASS 1024^3 block-scaled GEMM 126.57 TFLOP/s",
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, x_h, segs, gu_h, (wq, wf1, wf2))
+    print(json.dumps(result), flush=True)
+
+
+def _oracle_weight(oracle, wt):
+    """NVFP4 weight bytes from the oracle quantizer (untimed preparation; row
+    ranges on several host threads, the maximum over ranges is exact)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    N = wt.shape[0]
+    nthr = max(1, min(16, len(os.sched_getaffinity(0))))
+    step = (N + 4 * nthr - 1) // (4 * nthr)
+    ranges = [(a, min(N, a + step)) for a in range(0, N, step)]
+    with cf.ThreadPoolExecutor(nthr) as ex:
+        amax = max(ex.map(lambda r: oracle.bf16_amax(wt[r[0]:r[1]]), ranges))
+        sw = oracle.tensor_scale(amax)
+        parts = list(ex.map(lambda r: oracle.bf16_pack_rows(wt, sw, *r), ranges))
+    return sw, np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def cpu_baseline(args, x_h, segs, gu_h, works):
+    """The oracle as it stands, single-threaded, timed on a bounded sample of
+    the same step: for each projection, the producer (both passes) over its
+    first `cpu_rows` rows and the FP64 GEMM reference for those rows and all N.
+    Weight prepacking is not part of the step and is not timed."""
+    import numpy as np
+
+    import oracle
+
+    rows = args.cpu_rows
+    oracle.lib()
+    t_flop = t_bytes = t_prod = t_gemm = 0.0
+    for w in works:
+        sw, qw, sfw = _oracle_weight(oracle, w.weight())
+        t0 = time.perf_counter()
+        if w.kind == "modulate":
+            rs, sh, sc = w.segments()
+            seg = oracle.Segments(rs, sh, sc)
+            amax = oracle.modulate_amax_rows(x_h, seg, 0, rows)
+            s_g = oracle.tensor_scale(amax)
+            qa, sfa = oracle.modulate_pack_rows(x_h, seg, s_g, 0, rows)
+            t_bytes += 2 * rows * w.K * 2 + rows * (w.K // 2 + w.K // 16)
+        else:
+            amax = oracle.swiglu_amax_rows(gu_h, 0, rows)
+            s_g = oracle.tensor_scale(amax)
+            qa, sfa = oracle.swiglu_pack_rows(gu_h, s_g, 0, rows)
+            t_bytes += 2 * rows * 2 * w.K * 2 + rows * (w.K // 2 + w.K // 16)
+        t_prod += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_rows(qa, sfa, s_g, qw, sfw, sw, np.arange(rows))
+        t_gemm += time.perf_counter() - t0
+        t_flop += 2.0 * rows * w.N * w.K
+    total = t_prod + t_gemm
+    return {
+        "value": round(t_flop / total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {rows} rows of each of QKV, FC1, FC2: producer (amax + pack over those rows) and FP64 "
+                  f"GEMM reference for all N; {total:.1f} s single-threaded",
+        "producer_GBps": round(t_bytes / t_prod / 1e9, 4),
+        "gemm_TFLOPs": round(t_flop / t_gemm / 1e12, 6),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

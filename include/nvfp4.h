@@ -1,0 +1,184 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 activation producer and
+ * block-scaled GEMM.
+ *
+ * What is computed (page title, section):
+ *  - "NVFP4 Modulation Producer Fusion", Dataflow / Exactness Contract: the
+ *    producer reads the normalized BF16 activation twice, reproduces the
+ *    per-segment AdaLN modulation y = (x * (scale + 1)) + shift with BF16
+ *    rounding after each operation, reduces |y| to its absolute maximum in the
+ *    first pass, and writes packed QDATA and E4M3 block scales into
+ *    caller-owned buffers in the second; y never reaches memory.
+ *  - "NVFP4 Streaming Design", Numerical Constraint: one exact global BF16
+ *    absolute maximum, one FP32 tensor scale derived from it, one E4M3 block
+ *    scale per 16 values, E2M1 values quantized with both scales; no tile can
+ *    be packed before the global reduction completes (two passes).
+ *  - "FC2 NVFP4 Library Scheduling", Exact Operation: row-major packed
+ *    activation [M,K] times packed weight [N,K] to BF16 [M,N]; FP32 compute;
+ *    alpha = activation tensor scale * weight tensor scale, read from device
+ *    memory; no bias; 37,810 logical rows padded to 37,824; the FC2 producer
+ *    fuses an exact BF16 SwiGLU.
+ *
+ * The quantizer the pages leave open is fixed here as:
+ *   s_g = amax / 2688 (= 6 * 448), or 1 when amax == 0
+ *   sf  = E4M3(RN(RN(a16 / 6) / s_g)), nearest-even, saturating at 448
+ *   q   = E2M1(RN(y / RN(float(sf) * s_g))), nearest with ties to the even
+ *         code, saturating at +-6, sign kept; all 16 codes 0 when sf is 0
+ *         (or the NaN code)
+ * with every operation a correctly rounded binary32 operation (no FMA
+ * contraction, no flush-to-zero, no approximate reciprocal).
+ *
+ * Layouts (all row-major, bf16 given as uint16_t bit patterns):
+ *   x       [M, D]   bf16, row stride ldx elements
+ *   qdata   [M_pad, D/2]  uint8: byte j of a row holds element 2j in bits 3..0
+ *                         and element 2j+1 in bits 7..4
+ *   sfa     [M_pad, D/16] uint8 E4M3FN, one per 16 consecutive elements
+ *   rows M..M_pad-1 of qdata and sfa are written as zero.
+ *
+ * Conventions:
+ *  - Every pointer is device memory except nvfp4_segments.row_start (host).
+ *  - Buffers are caller-owned; the library allocates nothing and never
+ *    synchronizes the host.  Work is enqueued on `stream` (a hipStream_t
+ *    passed as void*; NULL = the null stream) in stream order, so
+ *    absmax -> pack -> gemm on one stream need no synchronization.
+ *  - Argument errors are reported synchronously, before anything is enqueued.
+ *    A launch failure returns NVFP4_ERR_HIP; nvfp4_last_hip_error() gives the
+ *    HIP error code of the calling thread's last failure.
+ *  - Data-dependent conditions are not reported: a non-finite input yields a
+ *    non-finite tensor scale, which the caller can test.
+ *  - Calls that share a workspace or outputs must not overlap in time (for
+ *    example on two streams without ordering between them).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, ld too small */
+    NVFP4_ERR_SHAPE = 2,            /* width not a multiple of 16 (64 for the GEMM's K), M_pad < pad64(M) */
+    NVFP4_ERR_ALIGNMENT = 3,        /* base pointer or stride breaks the 16-byte rule */
+    NVFP4_ERR_SEGMENTS = 4,         /* bad segment table */
+    NVFP4_ERR_HIP = 5               /* kernel launch failed */
+} nvfp4_status;
+
+/* Per-segment modulation parameters ("NVFP4 Modulation Producer Fusion",
+ * Exactness Contract: segment-specific shift and scale selection).  Segment s
+ * covers rows [row_start[s], row_start[s+1]); row_start has count+1 HOST
+ * entries with row_start[0] = 0, strictly increasing, row_start[count] = M,
+ * 1 <= count <= NVFP4_MAX_SEGMENTS.  shift and scale are DEVICE bf16 arrays
+ * [count, D] with row stride ld (>= D, multiple of 8, 16-byte aligned base). */
+#define NVFP4_MAX_SEGMENTS 16
+typedef struct {
+    int32_t count;
+    const int64_t* row_start;
+    const uint16_t* shift;
+    const uint16_t* scale;
+    int64_t ld;
+} nvfp4_segments;
+
+/* ceil(m / 64) * 64: the padded row count of QDATA/SFA (37,810 -> 37,824,
+ * "FC2 NVFP4 Library Scheduling", Exact Operation). */
+int64_t nvfp4_padded_rows(int64_t m);
+
+/* Bytes of device workspace the absmax passes need.  The workspace must be
+ * zero-filled once before its first use; every completed absmax call leaves
+ * it zero-filled again.  It must not be shared by calls that may overlap. */
+size_t nvfp4_absmax_workspace_bytes(void);
+
+/* Pass 1 of the modulation producer ("NVFP4 Modulation Producer Fusion",
+ * Dataflow, prototype step 1; "NVFP4 Streaming Design", Numerical Constraint,
+ * steps 1-2).  Computes y for every element of x [M, D] (row stride ldx, in
+ * elements), reduces max |y| over all M rows, and writes
+ *   *tensor_scale = amax == 0 ? 1 : RN(amax / 2688)   (device float)
+ *   *amax_out     = amax                              (device float, may be NULL)
+ * Requirements: M >= 1, D >= 16, D % 16 == 0, ldx >= D, ldx % 8 == 0, x
+ * 16-byte aligned; seg valid for M rows and width D. */
+nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                   const nvfp4_segments* seg, void* workspace,
+                                   float* tensor_scale, float* amax_out, void* stream);
+
+/* Pass 2 of the modulation producer ("NVFP4 Modulation Producer Fusion",
+ * Dataflow, prototype step 2; "NVFP4 Streaming Design", Numerical Constraint,
+ * steps 3-4).  Recomputes y and writes qdata [M_pad, D/2] and sfa
+ * [M_pad, D/16] using the device scalar *tensor_scale (normally written by
+ * nvfp4_modulate_absmax on the same stream).  Rows M..M_pad-1 are zero.
+ * Requirements as for absmax, plus M_pad >= nvfp4_padded_rows(M), qdata
+ * 16-byte aligned when D % 32 == 0 (else 8-byte), sfa 2-byte aligned. */
+nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                 const nvfp4_segments* seg, const float* tensor_scale,
+                                 uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);
+
+/* Pass 1 of the SwiGLU producer ("FC2 NVFP4 Library Scheduling", Exact
+ * Operation and Current Baseline: exact BF16 SwiGLU fused into NVFP4
+ * production).  h = bf16(bf16(silu(g)) * u) with silu(g) = g / (1 + exp(-g))
+ * in binary32 with a correctly rounded exp; g = gate[r*ld + c],
+ * u = up[r*ld + c] for c < F.  For one [M, 2F] gate/up tensor pass
+ * gate = GU, up = GU + F, ld = 2F.  Writes tensor scale and amax as
+ * nvfp4_modulate_absmax.  Requirements: F % 16 == 0, ld >= F, ld % 8 == 0,
+ * gate and up 16-byte aligned. */
+nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F,
+                                 int64_t ld, void* workspace, float* tensor_scale, float* amax_out,
+                                 void* stream);
+
+/* Pass 2 of the SwiGLU producer: recomputes h and writes qdata [M_pad, F/2]
+ * and sfa [M_pad, F/16] with the device *tensor_scale; pad rows zero. */
+nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F,
+                               int64_t ld, const float* tensor_scale, uint8_t* qdata, uint8_t* sfa,
+                               int64_t M_pad, void* stream);
+
+/* Block-scaled GEMM ("FC2 NVFP4 Library Scheduling", Exact Operation;
+ * "NVFP4 Streaming Design", P0: FP32 global-scale product applied before the
+ * BF16 conversion):
+ *   out[m][n] = bf16(RN(alpha * sum_k A[m][k] * W[n][k])),  m < M, n < N
+ *   A = e2m1(qa) * e4m3(sfa), W = e2m1(qw) * e4m3(sfw),
+ *   alpha = RN(*a_scale * *w_scale)  (both device floats)
+ * qa [M_pad, K/2], sfa [M_pad, K/16] (rows >= M are read as padding and
+ * ignored), qw [N, K/2], sfw [N, K/16], out [M, ldo] bf16.  The K sum is
+ * accumulated in binary32 in an order of the kernel's choosing.
+ * Requirements: K % 64 == 0, N % 16 == 0, ldo >= N, ldo % 4 == 0,
+ * M_pad >= M, qa/qw 16-byte aligned, sfa/sfw 4-byte aligned, out 8-byte
+ * aligned. */
+nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
+                        int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
+                        int64_t N, int64_t K, uint16_t* out, int64_t ldo, void* stream);
+
+/* ---- Single-step entry points ------------------------------------------
+ * Elementwise versions of single producer steps, running the very device
+ * functions the producer kernels use, so that each step can be checked over
+ * its whole input domain.  All arrays are device memory of n elements. */
+
+/* a1: y[i] = bf16(bf16(bf16(x*bf16(scale+1))) + shift)
+ * ("NVFP4 Modulation Producer Fusion", Exactness Contract). */
+nvfp4_status nvfp4_step_modulate(const uint16_t* x, const uint16_t* scale, const uint16_t* shift,
+                                 uint16_t* y, int64_t n, void* stream);
+/* a6: h[i] = bf16(bf16(silu(g)) * u) ("FC2 NVFP4 Library Scheduling"). */
+nvfp4_status nvfp4_step_swiglu(const uint16_t* g, const uint16_t* u, uint16_t* h, int64_t n,
+                               void* stream);
+/* a3: sf[i] = E4M3(RN(RN(a16[i] / 6) / *s_g)) with a16 given as bf16 bits
+ * ("NVFP4 Streaming Design", Numerical Constraint, step 3). */
+nvfp4_status nvfp4_step_block_scale(const uint16_t* a16, const float* s_g, uint8_t* sf, int64_t n,
+                                    void* stream);
+/* a4: code[i] = E2M1(RN(y[i] / RN(float(sf[i]) * *s_g))), 0 when sf[i] is 0
+ * or the NaN code ("NVFP4 Streaming Design", Numerical Constraint, step 4). */
+nvfp4_status nvfp4_step_element_code(const uint16_t* y, const uint8_t* sf, const float* s_g,
+                                     uint8_t* code, int64_t n, void* stream);
+/* E2M1 encoding of binary32 values (the conversion behind a4):
+ * code[i] = E2M1(v[i]) with ties to the even code and saturation at +-6. */
+nvfp4_status nvfp4_step_e2m1(const float* v, uint8_t* code, int64_t n, void* stream);
+/* E4M3 encoding of non-negative binary32 values (the conversion behind a3). */
+nvfp4_status nvfp4_step_e4m3(const float* t, uint8_t* code, int64_t n, void* stream);
+
+const char* nvfp4_status_string(nvfp4_status s);
+int nvfp4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

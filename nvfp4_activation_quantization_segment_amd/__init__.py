@@ -1,0 +1,255 @@
+"""Python binding of the MI355X NVFP4 activation producer and block-scaled GEMM.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libnvfp4.so`` (built in-tree by ``build.py``).  PyTorch provides device
+memory and the current stream.  There is no fallback: importing this package
+without the built library raises.
+
+Functions named like the C entry points (``nvfp4_modulate_absmax`` ...) take
+torch tensors and the same arguments as the C ABI (``include/nvfp4.h``);
+``modulate_quantize``, ``swiglu_quantize`` and ``gemm`` are conveniences that
+allocate their outputs with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that the library must share
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "misaligned pointer or stride",
+           4: "invalid segment table", 5: "HIP launch failure"}
+MAX_SEGMENTS = 16
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        msg = f"{fn}: {_STATUS.get(status, status)}"
+        if status == 5:
+            msg += f" (hip error {hip_error})"
+        super().__init__(msg)
+        self.status = status
+
+
+class Segments(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("row_start", ctypes.POINTER(ctypes.c_int64)),
+                ("shift", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("ld", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run nvfp4_activation_quantization_segment_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, V = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    SEG = ctypes.POINTER(Segments)
+    sigs = {
+        "nvfp4_padded_rows": (I64, [I64]),
+        "nvfp4_absmax_workspace_bytes": (ctypes.c_size_t, []),
+        "nvfp4_modulate_absmax": (I32, [P, I64, I64, I64, SEG, P, P, P, V]),
+        "nvfp4_modulate_pack": (I32, [P, I64, I64, I64, SEG, P, P, P, I64, V]),
+        "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
+        "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
+        "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
+        "nvfp4_step_modulate": (I32, [P, P, P, P, I64, V]),
+        "nvfp4_step_swiglu": (I32, [P, P, P, I64, V]),
+        "nvfp4_step_block_scale": (I32, [P, P, P, I64, V]),
+        "nvfp4_step_element_code": (I32, [P, P, P, P, I64, V]),
+        "nvfp4_step_e2m1": (I32, [P, P, I64, V]),
+        "nvfp4_step_e4m3": (I32, [P, P, I64, V]),
+        "nvfp4_status_string": (ctypes.c_char_p, [I32]),
+        "nvfp4_last_hip_error": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t) -> ctypes.c_void_p | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != NVFP4_OK:
+        raise Nvfp4Error(fn, status, lib.nvfp4_last_hip_error())
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected bf16 (or its 16-bit pattern), got {t.dtype}")
+    return t
+
+
+def make_segments(row_start, shift: torch.Tensor, scale: torch.Tensor):
+    """Build the C segment table; returns (struct, keepalive)."""
+    rs = (ctypes.c_int64 * len(row_start))(*[int(r) for r in row_start])
+    _bits16(shift)
+    _bits16(scale)
+    if shift.shape != scale.shape or shift.dim() != 2 or shift.stride(1) != 1 or scale.stride(0) != shift.stride(0):
+        raise ValueError("shift/scale must be [S, D] with unit column stride and equal row strides")
+    seg = Segments(len(row_start) - 1, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), shift.data_ptr(),
+                   scale.data_ptr(), shift.stride(0))
+    return seg, (rs, shift, scale)
+
+
+_workspaces: dict[int, torch.Tensor] = {}
+
+
+def workspace(device=None) -> torch.Tensor:
+    """Per-device zero-filled absmax workspace (left zeroed by every call)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(idx)
+    if ws is None:
+        ws = torch.zeros(int(lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
+        _workspaces[idx] = ws
+    return ws
+
+
+def padded_rows(m: int) -> int:
+    return int(lib.nvfp4_padded_rows(int(m)))
+
+
+# ---------------------------------------------------------------------------
+# C entry points, same names and arguments
+# ---------------------------------------------------------------------------
+def nvfp4_modulate_absmax(x, M, D, ldx, seg, ws, tensor_scale, amax_out=None, stream=None):
+    _check("nvfp4_modulate_absmax",
+           lib.nvfp4_modulate_absmax(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(ws), _ptr(tensor_scale),
+                                     _ptr(amax_out), _stream(stream)))
+
+
+def nvfp4_modulate_pack(x, M, D, ldx, seg, tensor_scale, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_modulate_pack",
+           lib.nvfp4_modulate_pack(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(tensor_scale), _ptr(qdata),
+                                   _ptr(sfa), M_pad, _stream(stream)))
+
+
+def nvfp4_swiglu_absmax(gate, up, M, F, ld, ws, tensor_scale, amax_out=None, stream=None):
+    _check("nvfp4_swiglu_absmax",
+           lib.nvfp4_swiglu_absmax(_ptr(gate), _ptr(up), M, F, ld, _ptr(ws), _ptr(tensor_scale), _ptr(amax_out),
+                                   _stream(stream)))
+
+
+def nvfp4_swiglu_pack(gate, up, M, F, ld, tensor_scale, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_swiglu_pack",
+           lib.nvfp4_swiglu_pack(_ptr(gate), _ptr(up), M, F, ld, _ptr(tensor_scale), _ptr(qdata), _ptr(sfa), M_pad,
+                                 _stream(stream)))
+
+
+def nvfp4_gemm(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, stream=None):
+    _check("nvfp4_gemm",
+           lib.nvfp4_gemm(_ptr(qa), _ptr(sfa), _ptr(a_scale), M, M_pad, _ptr(qw), _ptr(sfw), _ptr(w_scale), N, K,
+                          _ptr(out), ldo, _stream(stream)))
+
+
+def nvfp4_step_modulate(x, scale, shift, y, n, stream=None):
+    _check("nvfp4_step_modulate",
+           lib.nvfp4_step_modulate(_ptr(x), _ptr(scale), _ptr(shift), _ptr(y), n, _stream(stream)))
+
+
+def nvfp4_step_swiglu(g, u, h, n, stream=None):
+    _check("nvfp4_step_swiglu", lib.nvfp4_step_swiglu(_ptr(g), _ptr(u), _ptr(h), n, _stream(stream)))
+
+
+def nvfp4_step_block_scale(a16, s_g, sf, n, stream=None):
+    _check("nvfp4_step_block_scale", lib.nvfp4_step_block_scale(_ptr(a16), _ptr(s_g), _ptr(sf), n, _stream(stream)))
+
+
+def nvfp4_step_element_code(y, sf, s_g, code, n, stream=None):
+    _check("nvfp4_step_element_code",
+           lib.nvfp4_step_element_code(_ptr(y), _ptr(sf), _ptr(s_g), _ptr(code), n, _stream(stream)))
+
+
+def nvfp4_step_e2m1(v, code, n, stream=None):
+    _check("nvfp4_step_e2m1", lib.nvfp4_step_e2m1(_ptr(v), _ptr(code), n, _stream(stream)))
+
+
+def nvfp4_step_e4m3(t, code, n, stream=None):
+    _check("nvfp4_step_e4m3", lib.nvfp4_step_e4m3(_ptr(t), _ptr(code), n, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# conveniences (torch allocates the outputs)
+# ---------------------------------------------------------------------------
+def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: torch.Tensor, m_pad: int | None = None,
+                      stream=None):
+    """x [M, D] bf16 -> (qdata [M_pad, D/2] u8, sfa [M_pad, D/16] u8, tensor_scale f32[1], amax f32[1])."""
+    _bits16(x)
+    M, D = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    m_pad = padded_rows(M) if m_pad is None else m_pad
+    seg, keep = make_segments(row_start, shift, scale)
+    dev = x.device
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+    nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, stream)
+    nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, stream)
+    del keep
+    return q, s, ts, amax
+
+
+def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None):
+    """gate/up [M, 2F] bf16 (gate = first F columns) -> (qdata, sfa, tensor_scale, amax)."""
+    _bits16(gu)
+    M, F2 = gu.shape
+    F = F2 // 2
+    if gu.stride(1) != 1:
+        raise ValueError("gate/up must have unit column stride")
+    m_pad = padded_rows(M) if m_pad is None else m_pad
+    dev = gu.device
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    q = torch.empty((m_pad, F // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
+    up = gu.data_ptr() + F * gu.element_size()
+    nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, stream)
+    nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, stream)
+    return q, s, ts, amax
+
+
+def quantize_weight(w: torch.Tensor, stream=None):
+    """Prepack a bf16 weight [N, K] to NVFP4 with the identity modulation
+    (scale = +0, shift = -0): returns (qw [N, K/2], sfw [N, K/16], w_scale f32[1])."""
+    N, K = w.shape
+    shift = torch.full((1, K), -0.0, dtype=torch.bfloat16, device=w.device)
+    scale = torch.zeros((1, K), dtype=torch.bfloat16, device=w.device)
+    q, s, ts, _ = modulate_quantize(w, [0, N], shift, scale, stream=stream)
+    return q[:N], s[:N], ts
+
+
+def gemm(qa, sfa, a_scale, M: int, qw, sfw, w_scale, out: torch.Tensor | None = None, stream=None):
+    """out [M, N] bf16 = bf16(a_scale * w_scale * dequant(qa) dequant(qw)^T)."""
+    M_pad, Kh = qa.shape
+    N = qw.shape[0]
+    K = 2 * Kh
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    nvfp4_gemm(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, out.stride(0), stream)
+    return out

@@ -1,0 +1,217 @@
+// C ABI of the NVFP4 producer and GEMM: argument validation, launch geometry
+// and error reporting.  Every check happens before anything is enqueued.
+#include <string.h>
+
+#include "internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+nvfp4_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return NVFP4_OK;
+    g_last_hip_error = (int)e;
+    return NVFP4_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t pad64(int64_t m) { return (m + 63) / 64 * 64; }
+
+// Geometry of a row pass over [rows_total, width] with 8-column chunks.
+RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int target_wgs, int reverse) {
+    RowGeo g;
+    g.M = M;
+    g.rows_total = rows_total;
+    g.ldx = ld;
+    g.C8 = (int32_t)(width / 8);
+    g.J = (g.C8 + 1023) / 1024;
+    const int per = (g.C8 + g.J - 1) / g.J;
+    g.block = (per + 63) / 64 * 64;
+    int64_t rpw = (rows_total + target_wgs - 1) / target_wgs;
+    if (rpw < 1) rpw = 1;
+    g.rows_per_wg = (int32_t)rpw;
+    g.grid = (int32_t)((rows_total + rpw - 1) / rpw);
+    g.reverse = reverse;
+    return g;
+}
+
+constexpr int kTargetWgs = 1024;
+
+nvfp4_status check_segments(const nvfp4_segments* seg, int64_t M, int64_t D, SegParams* out) {
+    if (!seg || !seg->row_start || !seg->shift || !seg->scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (seg->count < 1 || seg->count > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_SEGMENTS;
+    if (seg->row_start[0] != 0 || seg->row_start[seg->count] != M) return NVFP4_ERR_SEGMENTS;
+    for (int s = 0; s < seg->count; ++s)
+        if (seg->row_start[s + 1] <= seg->row_start[s]) return NVFP4_ERR_SEGMENTS;
+    if (seg->ld < D) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (seg->ld % 8 != 0 || !aligned(seg->shift, 16) || !aligned(seg->scale, 16)) return NVFP4_ERR_ALIGNMENT;
+    memset(out, 0, sizeof(*out));
+    out->count = seg->count;
+    for (int s = 0; s <= seg->count; ++s) out->row_start[s] = seg->row_start[s];
+    out->shift = seg->shift;
+    out->scale = seg->scale;
+    out->ld = seg->ld;
+    return NVFP4_OK;
+}
+
+nvfp4_status check_rows(const void* x, int64_t M, int64_t D, int64_t ld) {
+    if (!x) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (M <= 0 || D <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (D % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (D / 8 > (int64_t)1 << 20) return NVFP4_ERR_SHAPE;
+    if (ld < D) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (ld % 8 != 0 || !aligned(x, 16)) return NVFP4_ERR_ALIGNMENT;
+    return NVFP4_OK;
+}
+
+nvfp4_status check_outputs(const uint8_t* qdata, const uint8_t* sfa, int64_t M, int64_t M_pad) {
+    if (!qdata || !sfa) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (M_pad < pad64(M)) return NVFP4_ERR_SHAPE;
+    if (!aligned(qdata, 4)) return NVFP4_ERR_ALIGNMENT;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4_padded_rows(int64_t m) { return m <= 0 ? 0 : pad64(m); }
+
+size_t nvfp4_absmax_workspace_bytes(void) { return 256; }
+
+const char* nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NVFP4_ERR_SHAPE: return "unsupported shape";
+    case NVFP4_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case NVFP4_ERR_SEGMENTS: return "invalid segment table";
+    case NVFP4_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+int nvfp4_last_hip_error(void) { return g_last_hip_error; }
+
+nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                   const nvfp4_segments* seg, void* workspace, float* tensor_scale,
+                                   float* amax_out, void* stream) {
+    nvfp4_status st = check_rows(x, M, D, ldx);
+    if (st != NVFP4_OK) return st;
+    SegParams sp;
+    if ((st = check_segments(seg, M, D, &sp)) != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    const RowGeo g = row_geo(M, M, D, ldx, kTargetWgs, 0);
+    return hip_status(launch_modulate_absmax(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out,
+                                             (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                 const nvfp4_segments* seg, const float* tensor_scale, uint8_t* qdata,
+                                 uint8_t* sfa, int64_t M_pad, void* stream) {
+    nvfp4_status st = check_rows(x, M, D, ldx);
+    if (st != NVFP4_OK) return st;
+    SegParams sp;
+    if ((st = check_segments(seg, M, D, &sp)) != NVFP4_OK) return st;
+    if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    const RowGeo g = row_geo(M, M_pad, D, ldx, kTargetWgs, 1);
+    return hip_status(launch_modulate_pack(x, g, sp, tensor_scale, qdata, sfa, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,
+                                 void* workspace, float* tensor_scale, float* amax_out, void* stream) {
+    nvfp4_status st = check_rows(gate, M, F, ld);
+    if (st != NVFP4_OK) return st;
+    if ((st = check_rows(up, M, F, ld)) != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    const RowGeo g = row_geo(M, M, F, ld, kTargetWgs, 0);
+    return hip_status(launch_swiglu_absmax(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out,
+                                           (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,
+                               const float* tensor_scale, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
+                               void* stream) {
+    nvfp4_status st = check_rows(gate, M, F, ld);
+    if (st != NVFP4_OK) return st;
+    if ((st = check_rows(up, M, F, ld)) != NVFP4_OK) return st;
+    if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    const RowGeo g = row_geo(M, M_pad, F, ld, kTargetWgs, 1);
+    return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
+                        const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N, int64_t K,
+                        uint16_t* out, int64_t ldo, void* stream) {
+    if (!qa || !sfa || !a_scale || !qw || !sfw || !w_scale || !out) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (M <= 0 || N <= 0 || K <= 0 || ldo < N || M_pad < M) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (K % 64 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
+    // 32-bit byte offsets inside the kernel
+    if (M_pad * (K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+    if (M_pad >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+    if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sfa, 4) || !aligned(sfw, 4) || !aligned(out, 8) ||
+        ldo % 4 != 0 || !aligned(a_scale, 4) || !aligned(w_scale, 4))
+        return NVFP4_ERR_ALIGNMENT;
+    GemmArgs a;
+    a.qa = qa;
+    a.sfa = sfa;
+    a.a_scale = a_scale;
+    a.qw = qw;
+    a.sfw = sfw;
+    a.w_scale = w_scale;
+    a.out = out;
+    a.ldo = ldo;
+    a.M = (int32_t)M;
+    a.M_pad = (int32_t)M_pad;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    return hip_status(launch_gemm(a, (hipStream_t)stream));
+}
+
+static nvfp4_status step(int which, const void* a, const void* b, const void* c, void* out, int64_t n,
+                         void* stream) {
+    if (n < 0 || !out || !a) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (n == 0) return NVFP4_OK;
+    return hip_status(launch_step(which, a, b, c, out, n, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_step_modulate(const uint16_t* x, const uint16_t* scale, const uint16_t* shift, uint16_t* y,
+                                 int64_t n, void* stream) {
+    if (!scale || !shift) return NVFP4_ERR_INVALID_ARGUMENT;
+    return step(STEP_MODULATE, x, scale, shift, y, n, stream);
+}
+
+nvfp4_status nvfp4_step_swiglu(const uint16_t* g, const uint16_t* u, uint16_t* h, int64_t n, void* stream) {
+    if (!u) return NVFP4_ERR_INVALID_ARGUMENT;
+    return step(STEP_SWIGLU, g, u, nullptr, h, n, stream);
+}
+
+nvfp4_status nvfp4_step_block_scale(const uint16_t* a16, const float* s_g, uint8_t* sf, int64_t n, void* stream) {
+    if (!s_g) return NVFP4_ERR_INVALID_ARGUMENT;
+    return step(STEP_BLOCK_SCALE, a16, s_g, nullptr, sf, n, stream);
+}
+
+nvfp4_status nvfp4_step_element_code(const uint16_t* y, const uint8_t* sf, const float* s_g, uint8_t* code,
+                                     int64_t n, void* stream) {
+    if (!sf || !s_g) return NVFP4_ERR_INVALID_ARGUMENT;
+    return step(STEP_ELEMENT_CODE, y, sf, s_g, code, n, stream);
+}
+
+nvfp4_status nvfp4_step_e2m1(const float* v, uint8_t* code, int64_t n, void* stream) {
+    return step(STEP_E2M1, v, nullptr, nullptr, code, n, stream);
+}
+
+nvfp4_status nvfp4_step_e4m3(const float* t, uint8_t* code, int64_t n, void* stream) {
+    return step(STEP_E4M3, t, nullptr, nullptr, code, n, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the API layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+// Segment table passed to the kernels by value.
+struct SegParams {
+    int32_t count;
+    int64_t row_start[NVFP4_MAX_SEGMENTS + 1];
+    const uint16_t* shift;
+    const uint16_t* scale;
+    int64_t ld;
+};
+
+// Row-pass geometry: each thread owns 8-column chunks c = threadIdx.x + j*block
+// (j < J) of rows [blockIdx*rows_per_wg, +rows_per_wg).
+struct RowGeo {
+    int64_t M;            // logical rows
+    int64_t rows_total;   // rows the grid covers (M, or M_pad when padding is written)
+    int64_t ldx;          // input row stride (elements)
+    int32_t C8;           // 8-column chunks per row
+    int32_t J;            // chunks per thread
+    int32_t rows_per_wg;
+    int32_t grid;
+    int32_t block;
+    int32_t reverse;      // pack pass walks row tiles last-to-first
+};
+
+enum StepKind { STEP_MODULATE, STEP_SWIGLU, STEP_BLOCK_SCALE, STEP_ELEMENT_CODE, STEP_E2M1, STEP_E4M3 };
+
+hipError_t launch_modulate_absmax(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
+                                  float* tensor_scale, float* amax_out, hipStream_t s);
+hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegParams& seg, const float* tensor_scale,
+                                uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
+                                float* tensor_scale, float* amax_out, hipStream_t s);
+hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,
+                              uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+hipError_t launch_step(int which, const void* a, const void* b, const void* c, void* out, int64_t n, hipStream_t s);
+
+struct GemmArgs {
+    const uint8_t* qa;
+    const uint8_t* sfa;
+    const float* a_scale;
+    const uint8_t* qw;
+    const uint8_t* sfw;
+    const float* w_scale;
+    uint16_t* out;
+    int64_t ldo;
+    int32_t M, M_pad, N, K;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace nvfp4

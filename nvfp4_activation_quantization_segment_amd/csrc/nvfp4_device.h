@@ -1,0 +1,222 @@
+// Device-side numerics of the NVFP4 producer for gfx950 (CDNA4).
+//
+// Every function here is a correctly rounded binary32 computation of one step
+// of the quantizer (no FMA contraction, no flush-to-zero), built from gfx950
+// instructions whose rounding is checked over the step's whole input domain by
+// the single-step entry points.
+//
+// Sources (page title, section):
+//   "NVFP4 Modulation Producer Fusion", Exactness Contract -- the BF16
+//     modulation (x * (scale + 1)) + shift with BF16 rounding.
+//   "NVFP4 Streaming Design", Numerical Constraint -- global amax, FP32 tensor
+//     scale, one E4M3 scale per 16 values, E2M1 values with both scales.
+//   "FC2 NVFP4 Library Scheduling", Current Baseline -- exact BF16 SwiGLU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// BF16 <-> binary32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two binary32 -> two bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32);
+// a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------------------
+// Modulation: y = bf16(bf16(x * s1) + shift) with s1 = bf16(scale + 1)
+// already formed.  Operates on two packed bf16 values.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float mod_scale1(uint16_t scale_bits) {
+    float s = __uint_as_float((uint32_t)scale_bits << 16) + 1.0f;
+    return bf16_lo(pack_bf16x2(s, s));
+}
+
+__device__ __forceinline__ uint32_t modulate2(uint32_t x2, float s1a, float s1b, float sha, float shb) {
+    uint32_t p = pack_bf16x2(bf16_lo(x2) * s1a, bf16_hi(x2) * s1b);
+    return pack_bf16x2(bf16_lo(p) + sha, bf16_hi(p) + shb);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU: h = bf16(bf16(silu(g)) * u), silu(g) = g / (1 + exp(-g)) with a
+// correctly rounded binary32 exp.  The binary64 exp rounded to binary32 is
+// the correctly rounded value for every bf16 g (the exact value is never
+// within the binary64 error of a binary32 rounding midpoint).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_bf16_value(float g) {
+    float e = (float)exp(-(double)g);
+    float den = 1.0f + e;
+    float sl = g / den;  // correctly rounded division
+    return bf16_lo(pack_bf16x2(sl, sl));
+}
+
+__device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2) {
+    float sa = silu_bf16_value(bf16_lo(g2));
+    float sb = silu_bf16_value(bf16_hi(g2));
+    return pack_bf16x2(sa * bf16_lo(u2), sb * bf16_hi(u2));
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN (bias 7, max 448, 0x7F = NaN)
+// ---------------------------------------------------------------------------
+// Non-negative t -> nearest E4M3 code, ties to even; t >= 448 -> 0x7E;
+// NaN -> 0x7F.  Normals round the binary32 mantissa to 3 bits in integer
+// arithmetic; below 2^-6 the code is the integer nearest t * 2^9 (the E4M3
+// subnormal step), formed by adding 2^23 in binary32.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+    uint32_t u = __float_as_uint(t);
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    uint32_t code_n = (r >> 20) - (120u << 3);
+    float s = t * 512.0f;
+    s = s + 8388608.0f;
+    uint32_t code_s = __float_as_uint(s) - 0x4B000000u;
+    uint32_t code = (t < 0.015625f) ? code_s : code_n;
+    code = (t >= 448.0f) ? 0x7Eu : code;
+    code = ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7Fu : code;
+    return code;
+}
+
+// E4M3 code (0..0x7E) -> its binary32 value (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    float vn = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
+    float vs = (float)(c & 7u) * 0.001953125f;
+    return (c & 0x78u) ? vn : vs;
+}
+
+// ---------------------------------------------------------------------------
+// Division by a block constant.
+// For a correctly rounded reciprocal r = RN(1/d), the Markstein sequence
+//   q0 = RN(y*r); e = RN(q0*d - y) (exact, one fma); q = RN(q0 - e*r)
+// returns RN(y/d) whenever no intermediate overflows or underflows
+// (P. Markstein, IBM J. Res. Dev. 34(1), 1990).  The residual is formed as
+// q0*d - y rather than y - q0*d so that y = -0 yields -0 (an exact zero
+// residual then enters as -0 and cannot flip the sign of q0).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_markstein(float y, float d, float r) {
+    float q0 = y * r;
+    float e = __builtin_fmaf(q0, d, -y);
+    return __builtin_fmaf(-e, r, q0);
+}
+
+// RN(1/6) in binary32.
+constexpr float kRcp6 = 0x1.555556p-3f;
+
+// Block scale from the block maximum: E4M3(RN(RN(a16/6)/s_g)).  rg = RN(1/s_g).
+// Valid for finite a16 >= 0 and s_g in the kernel's fast range.  Inside a
+// tensor t <= 448 (up to rounding), but for an a16 far above 2688*s_g the
+// first product may overflow; any t >= 1024 saturates to 448 anyway, so the
+// uncorrected product is used there.
+__device__ __forceinline__ uint32_t block_scale_fast(float a16, float s_g, float rg) {
+    const float u = div_markstein(a16, 6.0f, kRcp6);
+    const float q0 = u * rg;
+    const float e = __builtin_fmaf(q0, s_g, -u);
+    const float t = (q0 >= 1024.0f) ? q0 : __builtin_fmaf(-e, rg, q0);
+    return e4m3_encode(t);
+}
+
+// Reference-form block scale with two correctly rounded divisions (any input).
+__device__ __forceinline__ uint32_t block_scale_slow(float a16, float s_g) {
+    float u = a16 / 6.0f;
+    float t = u / s_g;
+    return e4m3_encode(t);
+}
+
+// The fast path holds for 2^-80 <= s_g <= 2^100: every divisor and
+// reciprocal is a normal number and the Markstein residuals of the quotients
+// that decide a code are exact.
+__device__ __forceinline__ bool scale_in_fast_range(float s_g) {
+    return s_g >= 0x1p-80f && s_g <= 0x1p100f;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 (FP4).  v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds binary32 to
+// E2M1 with ties to the even code and saturates at +-6, keeping the sign;
+// byte `sel` of `old` receives (code(a) | code(b) << 4).
+// ---------------------------------------------------------------------------
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Codes for 8 consecutive bf16 values (4 packed words) of one block:
+// element 2j in the low nibble of byte j.  d = RN(sf*s_g), r = RN(1/d).
+// `fast` selects the Markstein quotient; otherwise correctly rounded division
+// with a NaN quotient mapped to code 0.
+__device__ __forceinline__ uint32_t quantize8(const uint32_t y[4], float d, float r, bool fast) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_lo(y[j]);
+        v[2 * j + 1] = bf16_hi(y[j]);
+    }
+    float q[8];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div_markstein(v[i], d, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float t = v[i] / d;
+            q[i] = (t != t) ? 0.0f : t;
+        }
+    }
+    uint32_t w = 0;
+    w = fp4_pack2<0>(w, q[0], q[1]);
+    w = fp4_pack2<1>(w, q[2], q[3]);
+    w = fp4_pack2<2>(w, q[4], q[5]);
+    w = fp4_pack2<3>(w, q[6], q[7]);
+    return w;
+}
+
+// Everything one block needs after its maximum is known.
+struct BlockQ {
+    uint32_t sf;    // E4M3 code
+    float d;        // RN(sf * s_g)
+    float r;        // RN(1/d)
+    bool fast;      // Markstein path valid
+    uint32_t keep;  // 0 when the block is all-zero output (sf 0 or NaN code)
+};
+
+__device__ __forceinline__ BlockQ block_setup(uint32_t amax_bits16, float s_g, float rg, bool sg_fast) {
+    BlockQ b;
+    float a16 = __uint_as_float(amax_bits16 << 16);
+    bool finite = amax_bits16 < 0x7F80u;
+    b.fast = sg_fast && finite;
+    b.sf = b.fast ? block_scale_fast(a16, s_g, rg) : block_scale_slow(a16, s_g);
+    b.d = e4m3_value(b.sf) * s_g;
+    b.r = 1.0f / b.d;  // correctly rounded
+    b.keep = (b.sf == 0u || b.sf == 0x7Fu) ? 0u : 0xFFFFFFFFu;
+    return b;
+}
+
+// Packed per-half maximum of two words of two uint16 each (v_pk_max_u16).
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    u16x2 x = __builtin_bit_cast(u16x2, a);
+    u16x2 y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// |y| as bf16 magnitude bits for two packed values.  As unsigned integers these
+// order finite magnitudes like the values and rank Inf and NaN above them.
+__device__ __forceinline__ uint32_t mag2(uint32_t y2) { return y2 & 0x7FFF7FFFu; }
+
+// Running packed maximum of magnitudes -> one 16-bit maximum.
+__device__ __forceinline__ uint32_t fold_max(uint32_t m2) {
+    uint32_t lo = m2 & 0xFFFFu, hi = m2 >> 16;
+    return lo > hi ? lo : hi;
+}
+
+}  // namespace nvfp4

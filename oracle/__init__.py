@@ -65,6 +65,14 @@ _SIGS = {
     "ora_bf16_amax": (_F, [_P, _I64, _I64, _I64]),
     "ora_bf16_pack_rows": (None, [_P, _I64, _I64, _I64, _F, _I64, _I64, _P, _P]),
     "ora_gemm_rows": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _P, _I64, _P]),
+    "ora_modulate_amax_rows": (_F, [_P, _I64, _I64, _I32, _P, _P, _P, _I64, _I64, _I64]),
+    "ora_swiglu_amax_rows": (_F, [_P, _P, _I64, _I64, _I64, _I64]),
+    "ora_modulate_batch": (None, [_P, _P, _P, _I64, _P]),
+    "ora_swiglu_batch": (None, [_P, _P, _I64, _P]),
+    "ora_block_scale_batch": (None, [_P, _I64, _F, _P]),
+    "ora_element_code_batch": (None, [_P, _P, _I64, _F, _P]),
+    "ora_e2m1_encode_batch": (None, [_P, _I64, _P]),
+    "ora_e4m3_encode_batch": (None, [_P, _I64, _P]),
 }
 
 
@@ -176,6 +184,22 @@ def modulate_amax(x: np.ndarray, seg: Segments) -> float:
                                          _ptr(seg.shift), _ptr(seg.scale), seg.shift.shape[1]))
 
 
+def modulate_amax_rows(x: np.ndarray, seg: Segments, r0: int, r1: int) -> float:
+    """max |y| over rows [r0, r1) of x (row indices of the full tensor)."""
+    x = _c(x, np.uint16)
+    M, D = x.shape
+    return float(lib().ora_modulate_amax_rows(_ptr(x), D, D, seg.count, _ptr(seg.row_start), _ptr(seg.shift),
+                                              _ptr(seg.scale), seg.shift.shape[1], r0, r1))
+
+
+def swiglu_amax_rows(gu: np.ndarray, r0: int, r1: int) -> float:
+    gu = _c(gu, np.uint16)
+    M, F2 = gu.shape
+    F = F2 // 2
+    base = gu.ctypes.data
+    return float(lib().ora_swiglu_amax_rows(ctypes.c_void_p(base), ctypes.c_void_p(base + 2 * F), F, F2, r0, r1))
+
+
 def modulate_pack_rows(x: np.ndarray, seg: Segments, s_g: float, r0: int, r1: int):
     x = _c(x, np.uint16)
     M, D = x.shape
@@ -282,3 +306,49 @@ def gemm_tolerance_ok(gpu: np.ndarray, ref: np.ndarray):
         ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
     worst = float(ratio.max()) if ratio.size else 0.0
     return bool(np.all(err <= bound)), worst
+
+
+# --------------------------------------------------------------------------
+# elementwise batches
+# --------------------------------------------------------------------------
+def modulate_batch(x, scale, shift) -> np.ndarray:
+    x, scale, shift = (_c(a, np.uint16).ravel() for a in (x, scale, shift))
+    y = np.empty(x.size, np.uint16)
+    lib().ora_modulate_batch(_ptr(x), _ptr(scale), _ptr(shift), x.size, _ptr(y))
+    return y
+
+
+def swiglu_batch(g, u) -> np.ndarray:
+    g, u = (_c(a, np.uint16).ravel() for a in (g, u))
+    h = np.empty(g.size, np.uint16)
+    lib().ora_swiglu_batch(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def block_scale_batch(a16_bits, s_g: float) -> np.ndarray:
+    a = _c(a16_bits, np.uint16).ravel()
+    out = np.empty(a.size, np.uint8)
+    lib().ora_block_scale_batch(_ptr(a), a.size, float(np.float32(s_g)), _ptr(out))
+    return out
+
+
+def element_code_batch(y, sf, s_g: float) -> np.ndarray:
+    y = _c(y, np.uint16).ravel()
+    sf = _c(sf, np.uint8).ravel()
+    out = np.empty(y.size, np.uint8)
+    lib().ora_element_code_batch(_ptr(y), _ptr(sf), y.size, float(np.float32(s_g)), _ptr(out))
+    return out
+
+
+def e2m1_batch(v) -> np.ndarray:
+    v = _c(v, np.float32).ravel()
+    out = np.empty(v.size, np.uint8)
+    lib().ora_e2m1_encode_batch(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_batch(t) -> np.ndarray:
+    t = _c(t, np.float32).ravel()
+    out = np.empty(t.size, np.uint8)
+    lib().ora_e4m3_encode_batch(_ptr(t), t.size, _ptr(out))
+    return out

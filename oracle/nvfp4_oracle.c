@@ -211,8 +211,15 @@ static void pack_block(const uint16_t y[16], float s_g, uint8_t* q8, uint8_t* sf
 float ora_modulate_amax(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                         int32_t nseg, const int64_t* row_start,
                         const uint16_t* shift, const uint16_t* scale, int64_t ld_seg) {
+    return ora_modulate_amax_rows(x, D, ldx, nseg, row_start, shift, scale, ld_seg, 0, M);
+}
+
+float ora_modulate_amax_rows(const uint16_t* x, int64_t D, int64_t ldx,
+                             int32_t nseg, const int64_t* row_start,
+                             const uint16_t* shift, const uint16_t* scale, int64_t ld_seg,
+                             int64_t r0, int64_t r1) {
     uint16_t m = 0;
-    for (int64_t r = 0; r < M; ++r) {
+    for (int64_t r = r0; r < r1; ++r) {
         int32_t s = segment_of(r, nseg, row_start);
         for (int64_t c = 0; c < D; ++c) {
             uint16_t y = ora_modulate(x[r * ldx + c], scale[s * ld_seg + c], shift[s * ld_seg + c]);
@@ -248,8 +255,12 @@ void ora_modulate_pack_rows(const uint16_t* x, int64_t M, int64_t D, int64_t ldx
 }
 
 float ora_swiglu_amax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld) {
+    return ora_swiglu_amax_rows(gate, up, F, ld, 0, M);
+}
+
+float ora_swiglu_amax_rows(const uint16_t* gate, const uint16_t* up, int64_t F, int64_t ld, int64_t r0, int64_t r1) {
     uint16_t m = 0;
-    for (int64_t r = 0; r < M; ++r)
+    for (int64_t r = r0; r < r1; ++r)
         for (int64_t c = 0; c < F; ++c) {
             uint16_t h = ora_swiglu(gate[r * ld + c], up[r * ld + c]);
             if (mag16(h) > m) m = mag16(h);
@@ -298,6 +309,34 @@ void ora_bf16_pack_rows(const uint16_t* y, int64_t M, int64_t D, int64_t ldy, fl
         }
         for (int64_t b = 0; b < D / 16; ++b) pack_block(y + r * ldy + b * 16, s_g, qrow + b * 8, srow + b);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Elementwise batches                                                       */
+/* ------------------------------------------------------------------------ */
+void ora_modulate_batch(const uint16_t* x, const uint16_t* scale, const uint16_t* shift, int64_t n, uint16_t* y) {
+    for (int64_t i = 0; i < n; ++i) y[i] = ora_modulate(x[i], scale[i], shift[i]);
+}
+
+void ora_swiglu_batch(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* h) {
+    for (int64_t i = 0; i < n; ++i) h[i] = ora_swiglu(g[i], u[i]);
+}
+
+/* a16 given as bf16 bits; its magnitude is used. */
+void ora_block_scale_batch(const uint16_t* a16, int64_t n, float s_g, uint8_t* sf) {
+    for (int64_t i = 0; i < n; ++i) sf[i] = ora_block_scale(ora_bf16_to_f32(mag16(a16[i])), s_g);
+}
+
+void ora_element_code_batch(const uint16_t* y, const uint8_t* sf, int64_t n, float s_g, uint8_t* code) {
+    for (int64_t i = 0; i < n; ++i) code[i] = ora_element_code(y[i], sf[i], s_g);
+}
+
+void ora_e2m1_encode_batch(const float* v, int64_t n, uint8_t* code) {
+    for (int64_t i = 0; i < n; ++i) code[i] = ora_e2m1_encode(v[i]);
+}
+
+void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code) {
+    for (int64_t i = 0; i < n; ++i) code[i] = ora_e4m3_encode(t[i]);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -62,6 +62,11 @@ uint8_t  ora_element_code(uint16_t y, uint8_t sf, float s_g);   /* E2M1(RN(y/RN(
 float ora_modulate_amax(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                         int32_t nseg, const int64_t* row_start,
                         const uint16_t* shift, const uint16_t* scale, int64_t ld_seg);
+/* max |y| over rows [r0, r1) only (the full maximum is the max over row ranges). */
+float ora_modulate_amax_rows(const uint16_t* x, int64_t D, int64_t ldx,
+                             int32_t nseg, const int64_t* row_start,
+                             const uint16_t* shift, const uint16_t* scale, int64_t ld_seg,
+                             int64_t r0, int64_t r1);
 /* Writes rows [r0, r1) of qdata [*, D/2] and sfa [*, D/16]; rows >= M are zero-filled. */
 void ora_modulate_pack_rows(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                             int32_t nseg, const int64_t* row_start,
@@ -70,12 +75,21 @@ void ora_modulate_pack_rows(const uint16_t* x, int64_t M, int64_t D, int64_t ldx
                             uint8_t* qdata, uint8_t* sfa);
 /* gate/up: [M, F] bf16 views with row stride ld (for one [M, 2F] tensor: up = gate + F, ld = 2F). */
 float ora_swiglu_amax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld);
+float ora_swiglu_amax_rows(const uint16_t* gate, const uint16_t* up, int64_t F, int64_t ld, int64_t r0, int64_t r1);
 void  ora_swiglu_pack_rows(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,
                            float s_g, int64_t r0, int64_t r1, uint8_t* qdata, uint8_t* sfa);
 /* Quantize an already-formed bf16 tensor y [M, D] (row stride ldy). */
 float ora_bf16_amax(const uint16_t* y, int64_t M, int64_t D, int64_t ldy);
 void  ora_bf16_pack_rows(const uint16_t* y, int64_t M, int64_t D, int64_t ldy, float s_g,
                          int64_t r0, int64_t r1, uint8_t* qdata, uint8_t* sfa);
+
+/* ---- elementwise batches (plain loops over the scalar steps) --------- */
+void ora_modulate_batch(const uint16_t* x, const uint16_t* scale, const uint16_t* shift, int64_t n, uint16_t* y);
+void ora_swiglu_batch(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* h);
+void ora_block_scale_batch(const uint16_t* a16, int64_t n, float s_g, uint8_t* sf);
+void ora_element_code_batch(const uint16_t* y, const uint8_t* sf, int64_t n, float s_g, uint8_t* code);
+void ora_e2m1_encode_batch(const float* v, int64_t n, uint8_t* code);
+void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code);
 
 /* ---- GEMM reference ----------------------------------------------------- *
  * out[i][n] = (double)RN32(a_scale*w_scale) * sum_k A[rows[i]][k] * W[n][k]

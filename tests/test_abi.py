@@ -1,0 +1,96 @@
+"""The C ABI library: it loads, exports every entry point its header declares,
+and rejects bad arguments synchronously without launching anything (CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    import nvfp4_activation_quantization_segment_amd as m
+
+    return m
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("nvfp4_modulate_absmax", "nvfp4_modulate_pack", "nvfp4_swiglu_absmax", "nvfp4_swiglu_pack",
+              "nvfp4_gemm", "nvfp4_padded_rows", "nvfp4_absmax_workspace_bytes"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(pkg):
+    L = ctypes.CDLL(pkg.LIB_PATH)
+    missing = [s for s in declared_symbols() if not hasattr(L, s)]
+    assert not missing, missing
+
+
+def test_library_is_hip_code_for_gfx950(pkg):
+    data = open(pkg.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_padded_rows_and_workspace(pkg):
+    assert pkg.lib.nvfp4_padded_rows(37810) == 37824
+    assert pkg.lib.nvfp4_padded_rows(64) == 64
+    assert pkg.lib.nvfp4_padded_rows(1) == 64
+    assert pkg.lib.nvfp4_absmax_workspace_bytes() >= 8
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+def _seg(pkg, rows, count=1, ld=64, shift=FAKE, scale=FAKE):
+    rs = (ctypes.c_int64 * (count + 1))(*rows)
+    return pkg.Segments(count, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), shift, scale, ld), rs
+
+
+def test_gemm_argument_errors(pkg):
+    g = pkg.lib.nvfp4_gemm
+    P = FAKE
+    assert g(None, P, P, 10, 64, P, P, P, 64, 64, P, 64, None) == 1
+    assert g(P, P, P, 0, 64, P, P, P, 64, 64, P, 64, None) == 1
+    assert g(P, P, P, 10, 64, P, P, P, 64, 48, P, 64, None) == 2       # K % 64
+    assert g(P, P, P, 10, 64, P, P, P, 40, 64, P, 64, None) == 2       # N % 16
+    assert g(P, P, P, 10, 8, P, P, P, 64, 64, P, 64, None) == 1        # M_pad < M
+    assert g(P, P, P, 10, 64, P, P, P, 64, 64, P, 32, None) == 1       # ldo < N
+    assert g(P + 4, P, P, 10, 64, P, P, P, 64, 64, P, 64, None) == 3   # qa alignment
+    assert g(P, P, P, 10, 64, P, P, P, 64, 64, P + 2, 64, None) == 3   # out alignment
+    assert g(P, P, P, 10, 64, P, P, P, 64, 64, P, 66, None) == 3       # ldo % 4
+
+
+def test_producer_argument_errors(pkg):
+    L = pkg.lib
+    seg, keep = _seg(pkg, [0, 10])
+    ws = ts = q = s = FAKE
+    assert L.nvfp4_modulate_absmax(None, 10, 64, 64, ctypes.byref(seg), ws, ts, None, None) == 1
+    assert L.nvfp4_modulate_absmax(FAKE, 10, 40, 40, ctypes.byref(seg), ws, ts, None, None) == 2   # D % 16
+    assert L.nvfp4_modulate_absmax(FAKE, 10, 64, 60, ctypes.byref(seg), ws, ts, None, None) == 1   # ldx < D
+    assert L.nvfp4_modulate_absmax(FAKE, 10, 64, 68, ctypes.byref(seg), ws, ts, None, None) == 3   # ldx % 8
+    assert L.nvfp4_modulate_absmax(FAKE + 8, 10, 64, 64, ctypes.byref(seg), ws, ts, None, None) == 3
+    bad, keep2 = _seg(pkg, [0, 9])
+    assert L.nvfp4_modulate_absmax(FAKE, 10, 64, 64, ctypes.byref(bad), ws, ts, None, None) == 4
+    bad2, keep3 = _seg(pkg, [0, 5, 5, 10], count=3)
+    assert L.nvfp4_modulate_absmax(FAKE, 10, 64, 64, ctypes.byref(bad2), ws, ts, None, None) == 4
+    many, keep4 = _seg(pkg, list(range(18)), count=17)
+    assert L.nvfp4_modulate_absmax(FAKE, 17, 64, 64, ctypes.byref(many), ws, ts, None, None) == 4
+    assert L.nvfp4_modulate_pack(FAKE, 10, 64, 64, ctypes.byref(seg), ts, q, s, 32, None) == 2     # M_pad
+    assert L.nvfp4_modulate_pack(FAKE, 10, 64, 64, ctypes.byref(seg), ts, q + 1, s, 64, None) == 3
+    assert L.nvfp4_swiglu_absmax(FAKE, FAKE, 10, 24, 48, ws, ts, None, None) == 2
+    assert L.nvfp4_swiglu_pack(FAKE, None, 10, 32, 64, ts, q, s, 64, None) == 1
+
+
+def test_status_strings(pkg):
+    for st in range(6):
+        assert pkg.lib.nvfp4_status_string(st)

@@ -1,0 +1,179 @@
+"""The block-scaled GEMM against the FP64 oracle:
+|gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref), ref = RN32(s_a*s_w) * sum_k A*W in
+binary64 (not rounded to bf16), rms over the checked outputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import _par
+from tests.gpu_util import device, host, host_u16, to_dev, to_dev_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import nvfp4_activation_quantization_segment_amd as pkg
+
+    device()
+    return pkg
+
+
+def bf16_np(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def out_f64(t):
+    return (host_u16(t).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check(ref, got, what=""):
+    ok, worst = oracle.gemm_tolerance_ok(got, ref)
+    assert ok, f"{what}: worst |err|/bound = {worst:.3g}"
+    return worst
+
+
+def oracle_quantized(a, w, m_pad):
+    sa, qa, sfa, _ = _par.quantize_bf16(a, m_pad)
+    sw, qw, sfw, _ = _par.quantize_bf16(w)
+    return sa, qa, sfa, sw, qw, sfw
+
+
+def gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M, ldo=None):
+    dev = device()
+    N = qw.shape[0]
+    ldo = N if ldo is None else ldo
+    out = torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device=dev)
+    m.nvfp4_gemm(to_dev(qa), to_dev(sfa), to_dev(np.array([sa], np.float32)), M, qa.shape[0], to_dev(qw),
+                 to_dev(sfw), to_dev(np.array([sw], np.float32)), N, 2 * qw.shape[1], out, ldo)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_tiny_workload_end_to_end_all_outputs(m):
+    """Tiny workload: GPU producer -> GPU GEMM, all 256 x 1024 outputs."""
+    w = synth.workload("tiny")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    W = w.weight()
+    q, s, ts, _ = m.modulate_quantize(to_dev_u16(x), rs, to_dev_u16(sh), to_dev_u16(sc))
+    qw, sfw, tw = m.quantize_weight(to_dev_u16(W))
+    out = m.gemm(q, s, ts, w.M, qw, sfw, tw)
+    torch.cuda.synchronize()
+    s_g, oq, osf, _ = oracle.modulate_quantize(x, oracle.Segments(rs, sh, sc))
+    sw, oqw, osfw, _ = oracle.quantize_bf16(W)
+    ref = _par.gemm_rows(oq, osf, s_g, oqw, osfw, sw, np.arange(w.M))
+    check(ref, out_f64(out), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 16, 64), (37, 48, 192), (300, 272, 128), (257, 1024, 512), (64, 16, 5376), (130, 528, 14336),
+])
+def test_ragged_shapes(m, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    m_pad = oracle.padded_rows(M)
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, m_pad)
+    out = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M)
+    ref = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    check(ref, out_f64(out), f"{M}x{N}x{K}")
+
+
+def test_output_stride_and_untouched_padding(m):
+    """ldo > N: the columns beyond N are not written."""
+    rng = np.random.default_rng(5)
+    M, N, K = 70, 64, 128
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, 128)
+    out = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M, ldo=N + 8)
+    got = out_f64(out)
+    assert np.isnan(got[:, N:]).all()
+    check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), got[:, :N])
+
+
+def test_identity_weight_returns_dequantized_activation(m):
+    rng = np.random.default_rng(6)
+    M, K = 96, 256
+    a = bf16_np(rng.standard_normal((M, K)))
+    eye = bf16_np(np.eye(K))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, eye, 128)
+    out = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M)
+    e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
+    codes = np.empty((M, K), np.int64)
+    codes[:, 0::2] = qa[:M] & 0xF
+    codes[:, 1::2] = qa[:M] >> 4
+    sf = np.array([oracle.e4m3_value(c) for c in range(256)])[sfa[:M]]
+    deq = e2[codes] * np.repeat(sf, 16, axis=1) * float(sa)
+    check(deq, out_f64(out), "identity")
+
+
+def test_zero_activation_gives_zero(m):
+    M, N, K = 64, 32, 64
+    qa = np.zeros((M, K // 2), np.uint8)
+    sfa = np.zeros((M, K // 16), np.uint8)
+    rng = np.random.default_rng(7)
+    w = bf16_np(rng.standard_normal((N, K)))
+    sw, qw, sfw, _ = _par.quantize_bf16(w)
+    out = gpu_gemm(m, 1.0, qa, sfa, sw, qw, sfw, M)
+    assert (out_f64(out) == 0).all()
+
+
+def test_extreme_scales_fp16_range(m):
+    """Largest and smallest decoded magnitudes (6*448 and 0.5*2^-9) on both
+    operands stay exact through the fp16 decode."""
+    M, N, K = 64, 16, 64
+    qa = np.full((M, K // 2), 0x77, np.uint8)     # +6, +6
+    sfa = np.full((M, K // 16), 0x7E, np.uint8)   # 448
+    qw = np.full((N, K // 2), 0x11, np.uint8)     # +0.5
+    sfw = np.full((N, K // 16), 0x01, np.uint8)   # 2^-9
+    out = gpu_gemm(m, 1.0, qa, sfa, 1.0, qw, sfw, M)
+    ref = _par.gemm_rows(qa, sfa, 1.0, qw, sfw, 1.0, np.arange(M))
+    assert np.allclose(ref, 2688.0 * 2.0 ** -10 * K)
+    check(ref, out_f64(out), "extremes")
+
+
+@pytest.mark.parametrize("name", ["qkv", "fc1", "fc2"])
+def test_canonical_projection_sampled_rows(m, name):
+    """Producer + GEMM at M = 37,810 on one stream; 64 checked rows (boundary
+    rows 0, 1, 63, 64, 30999, 31000, 37807-37809 plus seeded rows), all N."""
+    w = synth.workload(name)
+    dev = device()
+    print(f"{name}: M={w.M} K={w.K} N={w.N}", flush=True)
+    if w.kind == "modulate":
+        x = w.x()
+        rs, sh, sc = w.segments()
+        q, s, ts, _ = m.modulate_quantize(to_dev_u16(x), rs, to_dev_u16(sh), to_dev_u16(sc))
+    else:
+        gu = w.gate_up()
+        q, s, ts, _ = m.swiglu_quantize(to_dev_u16(gu))
+    W = w.weight()
+    qw, sfw, tw = m.quantize_weight(to_dev_u16(W))
+    out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    m.gemm(q, s, ts, w.M, qw, sfw, tw, out=out)
+    torch.cuda.synchronize()
+    rows = w.check_rows(64)
+    # oracle side: its own tensor scale over every row, its own bytes for the
+    # checked rows, its own weight quantization
+    if w.kind == "modulate":
+        seg = oracle.Segments(rs, sh, sc)
+        amax = max(_par._map(lambda r: oracle.modulate_amax_rows(x, seg, *r), _par._ranges(w.M, 64)))
+        sa = oracle.tensor_scale(amax)
+        parts = _par._map(lambda r: oracle.modulate_pack_rows(x, seg, sa, r, r + 1), list(rows))
+    else:
+        amax = max(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(w.M, 64)))
+        sa = oracle.tensor_scale(amax)
+        parts = _par._map(lambda r: oracle.swiglu_pack_rows(gu, sa, r, r + 1), list(rows))
+    assert np.float32(sa) == host(ts)[0]
+    oqa = np.concatenate([p[0] for p in parts])
+    osfa = np.concatenate([p[1] for p in parts])
+    sw, oqw, osfw, _ = _par.quantize_bf16(W)
+    assert sw == host(tw)[0]
+    assert np.array_equal(oqw, host(qw)) and np.array_equal(osfw, host(sfw))
+    ref = _par.gemm_rows(oqa, osfa, sa, oqw, osfw, sw, np.arange(rows.size))
+    got = out_f64(out[torch.from_numpy(rows).to(dev)])
+    worst = check(ref, got, name)
+    print(f"{name}: worst err/bound {worst:.3g}", flush=True)

@@ -1,0 +1,261 @@
+"""The modulation and SwiGLU producers against the oracle: tensor scale bits,
+QDATA and SFA byte for byte (padding rows included), at small and ragged
+shapes, on adversarial values, and at the canonical 37,810-row sizes."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import _par
+from tests.gpu_util import device, first_mismatch, host, host_u16, to_dev, to_dev_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import nvfp4_activation_quantization_segment_amd as pkg
+
+    device()
+    return pkg
+
+
+def gpu_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None):
+    """Run both passes on the GPU; x may be given with a wider row stride."""
+    M, D = x.shape
+    if ldx is not None and ldx != D:
+        wide = np.zeros((M, ldx), np.uint16)
+        wide[:, :D] = x
+        xd = to_dev_u16(wide)[:, :D]
+    else:
+        xd = to_dev_u16(x)
+    q, s, ts, amax = m.modulate_quantize(xd, row_start, to_dev_u16(shift), to_dev_u16(scale), m_pad=m_pad)
+    torch.cuda.synchronize()
+    return host(ts)[0], host(q), host(s), host(amax)[0]
+
+
+def check_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None):
+    M = x.shape[0]
+    m_pad = oracle.padded_rows(M) if m_pad is None else m_pad
+    seg = oracle.Segments(row_start, shift, scale)
+    s_g, q, s, amax = _par.modulate_quantize(x, seg, m_pad)
+    gs, gq, gsf, gamax = gpu_modulate(m, x, row_start, shift, scale, m_pad, ldx)
+    assert np.float32(gamax).view(np.uint32) == np.float32(amax).view(np.uint32), (gamax, amax)
+    assert np.float32(gs).view(np.uint32) == np.float32(s_g).view(np.uint32), (gs, s_g)
+    assert np.array_equal(gsf, s), "SFA " + str(first_mismatch(gsf, s))
+    assert np.array_equal(gq, q), "QDATA " + str(first_mismatch(gq, q))
+    return s_g
+
+
+def check_values(m, y):
+    """Quantize a given bf16 tensor exactly: identity modulation (scale = +0,
+    shift = -0) makes y = x for every non-NaN x."""
+    D = y.shape[1]
+    return check_modulate(m, y, np.array([0, y.shape[0]], np.int64), np.full((1, D), 0x8000, np.uint16),
+                          np.zeros((1, D), np.uint16))
+
+
+def bf16_np(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+def test_tiny_workload_byte_exact(m):
+    w = synth.workload("tiny")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    check_modulate(m, x, rs, sh, sc)
+
+
+@pytest.mark.parametrize("M,D,segs,ldx", [
+    (1, 16, (0, 1), None),
+    (63, 48, (0, 10, 63), None),
+    (65, 528, (0, 1, 2, 64, 65), None),
+    (130, 8208, (0, 70, 130), None),          # 1026 chunks per row: two chunks per thread
+    (97, 5376, (0, 31, 97), 5392),            # strided rows
+    (300, 256, tuple(range(0, 300, 20)) + (300,), None),   # 15 segments
+    (40, 64, tuple(range(0, 16)) + (40,), None),            # 16 segments (the maximum)
+])
+def test_ragged_shapes_and_segments(m, M, D, segs, ldx):
+    rng = np.random.default_rng(M * 7 + D)
+    x = bf16_np(rng.standard_normal((M, D)) * np.where(rng.random((M, D)) < 0.01, 100.0, 1.0))
+    S = len(segs) - 1
+    sh = bf16_np(0.1 * rng.standard_normal((S, D)))
+    sc = bf16_np(0.1 * rng.standard_normal((S, D)))
+    check_modulate(m, x, np.array(segs, np.int64), sh, sc, ldx=ldx)
+
+
+def test_every_bf16_value_as_y(m):
+    """All 65,280 non-NaN bf16 patterns (infinities included) as y, 16 per block."""
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = vals[(vals & 0x7FFF) <= 0x7F80]
+    D = 512
+    rows = (vals.size + D - 1) // D
+    y = np.concatenate([vals, np.zeros(rows * D - vals.size, np.uint16)]).reshape(rows, D)
+    check_values(m, y)
+    # finite values only, clipped to a moderate maximum
+    y2 = y.copy()
+    big = (y2 & 0x7FFF) > 0x4700
+    y2[big] = 0x4700 | (y2[big] & 0x8000)
+    check_values(m, y2)
+
+
+def test_subnormal_block_scales_and_saturation(m):
+    """Blocks whose maximum is tiny next to the global one get E4M3-subnormal
+    scales, where quotients exceed 6 and saturate."""
+    D = 64
+    rng = np.random.default_rng(31)
+    y = bf16_np(np.array([rng.standard_normal(D) * 2.0 ** k for k in range(-24, 4)]))
+    y[0, 0] = bf16_np([1000.0])[0]
+    check_values(m, y)
+
+
+def test_zero_tensor_gives_unit_scale(m):
+    x = np.zeros((70, 32), np.uint16)
+    sh = np.zeros((1, 32), np.uint16)
+    sc = bf16_np(np.ones((1, 32)))
+    s_g = check_modulate(m, x, np.array([0, 70]), sh, sc)
+    assert s_g == 1.0
+
+
+def test_signed_zeros_and_tiny_values(m):
+    D = 32
+    y = np.zeros((4, D), np.uint16)
+    y[0, :] = 0x8000                       # -0 everywhere in a block next to a nonzero max
+    y[0, 16] = 0x3F80
+    y[1, :16] = 0x8001                     # smallest negative subnormal
+    y[1, 16:] = 0x0001
+    y[2, :] = bf16_np(np.linspace(-1e-3, 1e-3, D))
+    y[3, 0] = 0x4000
+    check_values(m, y)
+
+
+def test_tiny_global_maximum_uses_exact_division(m):
+    """A tensor whose maximum is so small that s_g is subnormal (outside the
+    fast division range) still matches byte for byte."""
+    rng = np.random.default_rng(33)
+    y = bf16_np(rng.standard_normal((8, 64)) * 1e-38)
+    check_values(m, y)
+    y = bf16_np(rng.standard_normal((8, 64)) * 1e30)
+    check_values(m, y)
+
+
+def test_workspace_resets_between_calls(m):
+    """Two absmax calls in a row on one workspace: the second sees only its own
+    tensor (a smaller maximum), and the workspace returns to zero."""
+    dev = device()
+    rs = [0, 64]
+    sh = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
+    sc = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
+    big = torch.full((64, 64), 100.0, dtype=torch.bfloat16, device=dev)
+    small = torch.full((64, 64), 2.0, dtype=torch.bfloat16, device=dev)
+    _, _, ts1, a1 = m.modulate_quantize(big, rs, sh, sc)
+    _, _, ts2, a2 = m.modulate_quantize(small, rs, sh, sc)
+    torch.cuda.synchronize()
+    assert host(a1)[0] == 100.0 and host(a2)[0] == 2.0
+    assert host(ts2)[0] == np.float32(2.0) / np.float32(2688.0)
+    assert not host(m.workspace(dev)).any()
+
+
+def test_non_default_stream(m):
+    w = synth.workload("tiny")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    seg = oracle.Segments(rs, sh, sc)
+    s_g, q, s, _ = oracle.modulate_quantize(x, seg)
+    st = torch.cuda.Stream()
+    xd, shd, scd = to_dev_u16(x), to_dev_u16(sh), to_dev_u16(sc)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        gq, gs, gts, _ = m.modulate_quantize(xd, rs, shd, scd, stream=st)
+    st.synchronize()
+    assert np.array_equal(host(gq), q) and np.array_equal(host(gs), s)
+    assert host(gts)[0] == s_g
+
+
+def test_weight_prepack_matches_oracle_quantizer(m):
+    w = synth.workload("tiny").weight()
+    sw, qw, sfw, _ = _par.quantize_bf16(w)
+    gq, gs, gts = m.quantize_weight(to_dev_u16(w))
+    torch.cuda.synchronize()
+    assert host(gts)[0] == sw
+    assert np.array_equal(host(gq), qw) and np.array_equal(host(gs), sfw)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU producer
+# --------------------------------------------------------------------------
+def check_swiglu(m, gu, m_pad=None):
+    M = gu.shape[0]
+    m_pad = oracle.padded_rows(M) if m_pad is None else m_pad
+    s_g, q, s, amax = _par.swiglu_quantize(gu, m_pad)
+    gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu), m_pad=m_pad)
+    torch.cuda.synchronize()
+    assert host(gamax)[0] == amax and host(gts)[0] == s_g
+    assert np.array_equal(host(gs), s), first_mismatch(host(gs), s)
+    assert np.array_equal(host(gq), q), first_mismatch(host(gq), q)
+
+
+@pytest.mark.parametrize("M,F", [(1, 16), (77, 48), (200, 512), (65, 8208)])
+def test_swiglu_small_shapes(m, M, F):
+    rng = np.random.default_rng(M + F)
+    gu = bf16_np(3 * rng.standard_normal((M, 2 * F)))
+    check_swiglu(m, gu)
+
+
+def test_swiglu_separate_gate_and_up_pointers(m):
+    """gate and up as two separate [M, F] tensors with their own stride."""
+    rng = np.random.default_rng(41)
+    M, F = 90, 96
+    g = bf16_np(2 * rng.standard_normal((M, F)))
+    u = bf16_np(rng.standard_normal((M, F)))
+    gu = np.concatenate([g, u], axis=1)
+    s_g, q, s, _ = _par.swiglu_quantize(gu, 128)
+    dev = device()
+    gd, ud = to_dev_u16(g), to_dev_u16(u)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    qd = torch.empty((128, F // 2), dtype=torch.uint8, device=dev)
+    sd = torch.empty((128, F // 16), dtype=torch.uint8, device=dev)
+    m.nvfp4_swiglu_absmax(gd, ud, M, F, F, m.workspace(dev), ts)
+    m.nvfp4_swiglu_pack(gd, ud, M, F, F, ts, qd, sd, 128)
+    torch.cuda.synchronize()
+    assert host(ts)[0] == s_g and np.array_equal(host(qd), q) and np.array_equal(host(sd), s)
+
+
+# --------------------------------------------------------------------------
+# canonical sizes
+# --------------------------------------------------------------------------
+def test_producer_canonical_37810_rows_byte_exact(m):
+    """The 37,810 x 5,376 producer workload, two segments, every row."""
+    w = synth.workload("producer")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    print(f"producer workload {x.shape}", flush=True)
+    s_g = check_modulate(m, x, rs, sh, sc)
+    assert s_g > 0
+
+
+def test_swiglu_canonical_37810_rows(m):
+    """The 37,810 x 2*14,336 FC2 producer: tensor scale over every row, QDATA
+    and SFA on all padding rows and on 2,048 sampled rows."""
+    w = synth.workload("fc2")
+    gu = w.gate_up()
+    M = w.M
+    print(f"swiglu workload {gu.shape}", flush=True)
+    gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu))
+    torch.cuda.synchronize()
+    amax = max(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(M, 64)))
+    s_g = oracle.tensor_scale(amax)
+    assert host(gamax)[0] == amax and host(gts)[0] == np.float32(s_g)
+    rows = np.unique(np.concatenate([synth.sample_rows(5, M, 2048, w.boundary_rows), np.arange(M, w.m_pad)]))
+    gq_h, gs_h = host(gq), host(gs)
+    for r0 in range(0, rows.size, 256):
+        rr = rows[r0:r0 + 256]
+        parts = _par._map(lambda r: oracle.swiglu_pack_rows(gu, s_g, r, r + 1), list(rr))
+        q = np.concatenate([p[0] for p in parts])
+        s = np.concatenate([p[1] for p in parts])
+        assert np.array_equal(gs_h[rr], s), first_mismatch(gs_h[rr], s)
+        assert np.array_equal(gq_h[rr], q), first_mismatch(gq_h[rr], q)

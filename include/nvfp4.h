@@ -109,8 +109,8 @@ nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int6
  * steps 3-4).  Recomputes y and writes qdata [M_pad, D/2] and sfa
  * [M_pad, D/16] using the device scalar *tensor_scale (normally written by
  * nvfp4_modulate_absmax on the same stream).  Rows M..M_pad-1 are zero.
- * Requirements as for absmax, plus M_pad >= nvfp4_padded_rows(M), qdata
- * 16-byte aligned when D % 32 == 0 (else 8-byte), sfa 2-byte aligned. */
+ * Requirements as for absmax, plus M_pad >= nvfp4_padded_rows(M) and qdata
+ * 4-byte aligned. */
 nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                                  const nvfp4_segments* seg, const float* tensor_scale,
                                  uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);

@@ -53,8 +53,116 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
     return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
+// LDS tiles: decoded fp16 [256 rows][64 k] per operand, row stride 72 halves
+// (144 bytes: 16 bytes of padding make the 32 rows read by one MFMA fragment
+// fall on distinct bank groups), two stages.
+constexpr int kLDK = kBK + 8;
+constexpr int kTileHalves = kBM * kLDK;  // per operand per stage
+constexpr int kLdsBytes = 2 /*stages*/ * 2 /*operands*/ * kTileHalves * 2;
+
+struct RowPack {
+    uint4 q0, q1;  // 64 nibbles of one row for one K step
+    uint32_t sc;   // its 4 block scales
+};
+
+__device__ __forceinline__ RowPack load_row(const uint8_t* q, const uint8_t* sf, uint32_t qoff, uint32_t soff) {
+    RowPack r;
+    r.q0 = *reinterpret_cast<const uint4*>(q + qoff);
+    r.q1 = *reinterpret_cast<const uint4*>(q + qoff + 16);
+    r.sc = *reinterpret_cast<const uint32_t*>(sf + soff);
+    return r;
+}
+
+// Decode one row's 64 values into LDS (8 x 16-byte stores).
+__device__ __forceinline__ void store_row(const RowPack& r, _Float16* dst) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t w = word_of(i < 4 ? r.q0 : r.q1, i & 3);
+        const f16x8 v = decode8(w, sf_raw2(r.sc, i >> 1));
+        *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
+    }
+}
+
+// Decode words 2p and 2p+1 of a staged row (16 values, block p>>... of the
+// row's 4 blocks) into LDS: two 16-byte stores.
+__device__ __forceinline__ void store_part(const RowPack& r, int p, _Float16* dst) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 2 * p + u;
+        const uint32_t w = word_of(i < 4 ? r.q0 : r.q1, i & 3);
+        *reinterpret_cast<f16x8*>(dst + 8 * i) = decode8(w, sf_raw2(r.sc, i >> 1));
+    }
+}
+
+// One K step on LDS buffer CUR, in four phases (one per 16-wide K slice j):
+// read the fragments of slice j+1, decode a quarter of the next stage's rows
+// (DECODE) into the other buffer, and issue the 16 MFMAs of slice j.  CUR is a
+// template parameter so that both buffers' offsets are constants and the reads
+// of one buffer and the writes of the other are visibly independent.  The
+// next stage's packed rows are fetched at the start of the step into `nxt`.
+template <int CUR, bool DECODE>
+__device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)[4][4], RowPack& ra, RowPack& rw,
+                                       const GemmArgs& a, uint32_t aoff, uint32_t aso, uint32_t woff,
+                                       uint32_t wso, int next_stage, int tid, int wrow0, int arow0, int h) {
+    const _Float16* cA = lds + CUR * kTileHalves;
+    const _Float16* cW = lds + (2 + CUR) * kTileHalves;
+    _Float16* dA = lds + (CUR ^ 1) * kTileHalves + tid * kLDK;
+    _Float16* dW = lds + (2 + (CUR ^ 1)) * kTileHalves + tid * kLDK;
+    RowPack na, nw;
+    if (DECODE) {
+        const uint32_t db = 32u * next_stage, ds = 4u * next_stage;
+        na = load_row(a.qa, a.sfa, aoff + db, aso + ds);
+        nw = load_row(a.qw, a.sfw, woff + db, wso + ds);
+    }
+    f16x8 wf[2][4], af[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wf[0][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + 8 * h);
+        af[0][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + 8 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int b = j & 1;
+        if (j < 3) {
+            const int kk = 16 * (j + 1) + 8 * h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wf[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + kk);
+                af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
+            }
+        }
+        if (DECODE) {
+            store_part(ra, j, dA);
+            store_part(rw, j, dW);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[b][i], af[b][k], acc[i][k], 0, 0, 0);
+        if (DECODE) {
+            // per MFMA about two decode VALU ops; LDS traffic spread out
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                if ((i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (DECODE) {
+        ra = na;
+        rw = nw;
+    }
+    __syncthreads();
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
 gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
+
     // Tile order: each XCD (workgroups are dealt round-robin over 8) takes a
     // contiguous range of tiles, walked in groups of 8 M-tiles so that the
     // workgroups resident on one XCD share activation and weight rows in L2.
@@ -69,23 +177,19 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
     const int tm = first_m + (logical % gsz) % gm;
     const int tn = (logical % gsz) / gm;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const uint32_t Kb = (uint32_t)a.K >> 1, Ks = (uint32_t)a.K >> 4;
 
-    uint32_t woff[4], aoff[4], wso[4], aso[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int n = tn * kBN + wn * kWN + i * 32 + l32;
-        n = n < a.N ? n : a.N - 1;
-        int m = tm * kBM + wm * kWM + i * 32 + l32;
-        m = m < a.M_pad ? m : a.M_pad - 1;
-        woff[i] = (uint32_t)n * Kb + 16u * h;
-        aoff[i] = (uint32_t)m * Kb + 16u * h;
-        wso[i] = (uint32_t)n * Ks;
-        aso[i] = (uint32_t)m * Ks;
-    }
+    // this thread stages activation row tid and weight row tid of the tile
+    int mrow = tm * kBM + tid;
+    mrow = mrow < a.M_pad ? mrow : a.M_pad - 1;
+    int nrow = tn * kBN + tid;
+    nrow = nrow < a.N ? nrow : a.N - 1;
+    const uint32_t aoff = (uint32_t)mrow * Kb, aso = (uint32_t)mrow * Ks;
+    const uint32_t woff = (uint32_t)nrow * Kb, wso = (uint32_t)nrow * Ks;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -93,53 +197,53 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[i][k] = (f32x16){0};
 
-    const int nit = a.K / kBK;
-    uint4 wq[4], aq[4];
-    uint32_t wsc[4], asc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wq[i] = *reinterpret_cast<const uint4*>(a.qw + woff[i]);
-        aq[i] = *reinterpret_cast<const uint4*>(a.qa + aoff[i]);
-        wsc[i] = *reinterpret_cast<const uint32_t*>(a.sfw + wso[i]);
-        asc[i] = *reinterpret_cast<const uint32_t*>(a.sfa + aso[i]);
-    }
+    // fragment rows read by this lane
+    const int wrow0 = wn * 128 + l32;  // weight rows (MFMA A operand)
+    const int arow0 = wm * 128 + l32;  // activation rows (MFMA B operand)
 
-    for (int it = 0; it < nit; ++it) {
-        uint4 wqn[4], aqn[4];
-        uint32_t wscn[4], ascn[4];
-        if (it + 1 < nit) {
-            const uint32_t db = 32u * (it + 1), ds = 4u * (it + 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wqn[i] = *reinterpret_cast<const uint4*>(a.qw + woff[i] + db);
-                aqn[i] = *reinterpret_cast<const uint4*>(a.qa + aoff[i] + db);
-                wscn[i] = *reinterpret_cast<const uint32_t*>(a.sfw + wso[i] + ds);
-                ascn[i] = *reinterpret_cast<const uint32_t*>(a.sfa + aso[i] + ds);
-            }
-        }
+    const int nit = a.K / kBK;
+    RowPack ra = load_row(a.qa, a.sfa, aoff, aso);
+    RowPack rw = load_row(a.qw, a.sfw, woff, wso);
+    store_row(ra, lds + tid * kLDK);
+    store_row(rw, lds + 2 * kTileHalves + tid * kLDK);
+    {
+        const int s1 = nit > 1 ? 1 : 0;
+        ra = load_row(a.qa, a.sfa, aoff + 32u * s1, aso + 4u * s1);
+        rw = load_row(a.qw, a.sfw, woff + 32u * s1, wso + 4u * s1);
+    }
+    __syncthreads();
+
+    // steps 0 .. nit-2 decode the next stage; the stage after that is fetched
+    // (clamped to the last stage, a harmless repeat at the end)
+    int it = 0;
+    for (; it + 2 <= nit - 1; it += 2) {
+        const int n2 = it + 2 < nit ? it + 2 : nit - 1;
+        const int n3 = it + 3 < nit ? it + 3 : nit - 1;
+        k_step<0, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, n2, tid, wrow0, arow0, h);
+        k_step<1, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, n3, tid, wrow0, arow0, h);
+    }
+    if (it < nit - 1) {
+        k_step<0, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, nit - 1, tid, wrow0, arow0, h);
+        ++it;
+    }
+    // last step: MFMAs only, on buffer (nit - 1) & 1
+    {
+        const _Float16* cA = lds + (it & 1) * kTileHalves;
+        const _Float16* cW = lds + (2 + (it & 1)) * kTileHalves;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int b = 2 * h + (j >> 1);
+            const int kk = 16 * j + 8 * h;
             f16x8 wf[4], af[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                wf[i] = decode8(word_of(wq[i], j), sf_raw2(wsc[i], b));
-                af[i] = decode8(word_of(aq[i], j), sf_raw2(asc[i], b));
+                wf[i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + kk);
+                af[i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[k], acc[i][k], 0, 0, 0);
-        }
-        if (it + 1 < nit) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wq[i] = wqn[i];
-                aq[i] = aqn[i];
-                wsc[i] = wscn[i];
-                asc[i] = ascn[i];
-            }
         }
     }
 

@@ -14,15 +14,18 @@
 // instruction applies exactly) followed by one v_pk_mul_f16 by the raw E4M3
 // bits reinterpreted as fp16 (equal to sf * 2^-8, subnormals included).
 //
-// Tiling.  A workgroup of 4 waves computes a 256x256 output tile; each wave a
-// 128x128 sub-tile as 4x4 v_mfma_f32_32x32x16_f16 tiles with 256 fp32
-// accumulators per lane.  The MFMA A operand is the weight (rows n) and the
-// B operand the activation (rows m), so each lane's accumulators hold four
-// consecutive n of one m and the epilogue stores 8 contiguous bytes.  Packed
-// data goes straight from global memory to registers: per K step of 64 a lane
-// reads 16 bytes (32 nibbles) of each of its 4 weight and 4 activation rows
-// and one 4-byte word of their scales; the K order inside the step is
-// permuted identically for both operands, which leaves the sum unchanged.
+// Tiling.  A workgroup of 8 waves (two per SIMD) computes a 256x256 output
+// tile; each wave a 128(M) x 64(N) sub-tile as 4x2 v_mfma_f32_32x32x16_f16
+// tiles with 128 fp32 accumulators per lane.  Every packed element is decoded
+// once per workgroup: thread t < 256 decodes activation row t, thread t >= 256
+// weight row t-256, 64 values per K step of 64, into double-buffered fp16
+// tiles in LDS (256 rows x 64, row stride 144 bytes so that the 32 rows one
+// MFMA fragment reads fall on distinct bank groups); the waves then read their
+// fragments with 16-byte LDS loads.  The MFMA A operand is the weight (rows
+// n) and the B operand the activation (rows m), so each lane's accumulators
+// hold four consecutive n of one m and the epilogue stores 8 contiguous bytes.
+// Two waves per SIMD let the hardware overlap one wave's decode and LDS work
+// with the other's MFMAs.
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -32,7 +35,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 128, kWN = 128;
+constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 128, kWN = 64;
 
 // Raw E4M3 bits of byte `b` of a scale word, as two fp16 equal to sf * 2^-8.
 __device__ __forceinline__ uint32_t sf_raw2(uint32_t word, int b) {
@@ -83,8 +86,8 @@ __device__ __forceinline__ void store_row(const RowPack& r, _Float16* dst) {
     }
 }
 
-// Decode words 2p and 2p+1 of a staged row (16 values, block p>>... of the
-// row's 4 blocks) into LDS: two 16-byte stores.
+// Decode words 2p and 2p+1 of a staged row (the 16 values of block p) into
+// LDS: two 16-byte stores.
 __device__ __forceinline__ void store_part(const RowPack& r, int p, _Float16* dst) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -95,71 +98,54 @@ __device__ __forceinline__ void store_part(const RowPack& r, int p, _Float16* ds
 }
 
 // One K step on LDS buffer CUR, in four phases (one per 16-wide K slice j):
-// read the fragments of slice j+1, decode a quarter of the next stage's rows
-// (DECODE) into the other buffer, and issue the 16 MFMAs of slice j.  CUR is a
-// template parameter so that both buffers' offsets are constants and the reads
-// of one buffer and the writes of the other are visibly independent.  The
-// next stage's packed rows are fetched at the start of the step into `nxt`.
+// read the fragments of slice j+1, decode a quarter of this thread's row of the
+// next stage (DECODE) into the other buffer, and issue the 8 MFMAs of slice j.
+// CUR is a template parameter so that both buffers' offsets are constants and
+// the reads of one buffer and the writes of the other are visibly independent.
+// The packed row of the stage after next is fetched at the start of the step.
 template <int CUR, bool DECODE>
-__device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)[4][4], RowPack& ra, RowPack& rw,
-                                       const GemmArgs& a, uint32_t aoff, uint32_t aso, uint32_t woff,
-                                       uint32_t wso, int next_stage, int tid, int wrow0, int arow0, int h) {
+__device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)[2][4], RowPack& ra,
+                                       const GemmArgs& a, uint32_t roff, uint32_t rso, const uint8_t* q,
+                                       const uint8_t* sf, int next_stage, int tid, int wrow0, int arow0, int h) {
     const _Float16* cA = lds + CUR * kTileHalves;
     const _Float16* cW = lds + (2 + CUR) * kTileHalves;
-    _Float16* dA = lds + (CUR ^ 1) * kTileHalves + tid * kLDK;
-    _Float16* dW = lds + (2 + (CUR ^ 1)) * kTileHalves + tid * kLDK;
-    RowPack na, nw;
+    // thread tid < 256 decodes activation row tid, else weight row tid-256
+    _Float16* dst = lds + ((tid < 256 ? 0 : 2) + (CUR ^ 1)) * kTileHalves + (tid & 255) * kLDK;
+    RowPack na;
     if (DECODE) {
         const uint32_t db = 32u * next_stage, ds = 4u * next_stage;
-        na = load_row(a.qa, a.sfa, aoff + db, aso + ds);
-        nw = load_row(a.qw, a.sfw, woff + db, wso + ds);
+        na = load_row(q, sf, roff + db, rso + ds);
     }
-    f16x8 wf[2][4], af[2][4];
+    f16x8 wf[2][2], af[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wf[0][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + 8 * h);
-        af[0][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + 8 * h);
-    }
+    for (int i = 0; i < 2; ++i) wf[0][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + 8 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + 8 * h);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int b = j & 1;
         if (j < 3) {
             const int kk = 16 * (j + 1) + 8 * h;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2; ++i)
                 wf[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + kk);
-                af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
-            }
-        }
-        if (DECODE) {
-            store_part(ra, j, dA);
-            store_part(rw, j, dW);
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
+                af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
+        }
+        if (DECODE) store_part(ra, j, dst);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[b][i], af[b][k], acc[i][k], 0, 0, 0);
-        if (DECODE) {
-            // per MFMA about two decode VALU ops; LDS traffic spread out
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-                if ((i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if ((i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-            }
-        }
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (DECODE) {
-        ra = na;
-        rw = nw;
-    }
+    if (DECODE) ra = na;
     __syncthreads();
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
 
@@ -179,68 +165,55 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, l32 = lane & 31;
     const uint32_t Kb = (uint32_t)a.K >> 1, Ks = (uint32_t)a.K >> 4;
+    const uint8_t* q = tid < 256 ? a.qa : a.qw;
+    const uint8_t* sf = tid < 256 ? a.sfa : a.sfw;
+    int row;
+    if (tid < 256) { row = tm * kBM + tid; row = row < a.M_pad ? row : a.M_pad - 1; }
+    else { row = tn * kBN + (tid - 256); row = row < a.N ? row : a.N - 1; }
+    const uint32_t roff = (uint32_t)row * Kb, rso = (uint32_t)row * Ks;
 
-    // this thread stages activation row tid and weight row tid of the tile
-    int mrow = tm * kBM + tid;
-    mrow = mrow < a.M_pad ? mrow : a.M_pad - 1;
-    int nrow = tn * kBN + tid;
-    nrow = nrow < a.N ? nrow : a.N - 1;
-    const uint32_t aoff = (uint32_t)mrow * Kb, aso = (uint32_t)mrow * Ks;
-    const uint32_t woff = (uint32_t)nrow * Kb, wso = (uint32_t)nrow * Ks;
-
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[i][k] = (f32x16){0};
-
-    // fragment rows read by this lane
-    const int wrow0 = wn * 128 + l32;  // weight rows (MFMA A operand)
-    const int arow0 = wm * 128 + l32;  // activation rows (MFMA B operand)
-
+    const int wrow0 = wn * 64 + l32;
+    const int arow0 = wm * 128 + l32;
     const int nit = a.K / kBK;
-    RowPack ra = load_row(a.qa, a.sfa, aoff, aso);
-    RowPack rw = load_row(a.qw, a.sfw, woff, wso);
-    store_row(ra, lds + tid * kLDK);
-    store_row(rw, lds + 2 * kTileHalves + tid * kLDK);
+    RowPack ra = load_row(q, sf, roff, rso);
+    store_row(ra, lds + (tid < 256 ? 0 : 2) * kTileHalves + (tid & 255) * kLDK);
     {
         const int s1 = nit > 1 ? 1 : 0;
-        ra = load_row(a.qa, a.sfa, aoff + 32u * s1, aso + 4u * s1);
-        rw = load_row(a.qw, a.sfw, woff + 32u * s1, wso + 4u * s1);
+        ra = load_row(q, sf, roff + 32u * s1, rso + 4u * s1);
     }
     __syncthreads();
-
-    // steps 0 .. nit-2 decode the next stage; the stage after that is fetched
-    // (clamped to the last stage, a harmless repeat at the end)
     int it = 0;
     for (; it + 2 <= nit - 1; it += 2) {
         const int n2 = it + 2 < nit ? it + 2 : nit - 1;
         const int n3 = it + 3 < nit ? it + 3 : nit - 1;
-        k_step<0, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, n2, tid, wrow0, arow0, h);
-        k_step<1, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, n3, tid, wrow0, arow0, h);
+        k_step<0, true>(lds, acc, ra, a, roff, rso, q, sf, n2, tid, wrow0, arow0, h);
+        k_step<1, true>(lds, acc, ra, a, roff, rso, q, sf, n3, tid, wrow0, arow0, h);
     }
     if (it < nit - 1) {
-        k_step<0, true>(lds, acc, ra, rw, a, aoff, aso, woff, wso, nit - 1, tid, wrow0, arow0, h);
+        k_step<0, true>(lds, acc, ra, a, roff, rso, q, sf, nit - 1, tid, wrow0, arow0, h);
         ++it;
     }
-    // last step: MFMAs only, on buffer (nit - 1) & 1
     {
         const _Float16* cA = lds + (it & 1) * kTileHalves;
         const _Float16* cW = lds + (2 + (it & 1)) * kTileHalves;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int kk = 16 * j + 8 * h;
-            f16x8 wf[4], af[4];
+            f16x8 wf[2], af[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                wf[i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + kk);
-                af[i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
-            }
+            for (int i = 0; i < 2; ++i) wf[i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + kk);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[k], acc[i][k], 0, 0, 0);
@@ -255,7 +228,7 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
         if (m >= a.M) continue;
         uint16_t* orow = a.out + (int64_t)m * a.ldo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = tn * kBN + wn * kWN + i * 32 + 8 * q + 4 * h;
@@ -273,7 +246,7 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int tiles_m = (a.M + kBM - 1) / kBM;
     const int tiles_n = (a.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL(gemm_kernel, dim3(tiles_m * tiles_n), dim3(256), 0, s, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL(gemm_kernel, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 

@@ -21,24 +21,30 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int64_t pad64(int64_t m) { return (m + 63) / 64 * 64; }
 
 // Geometry of a row pass over [rows_total, width] with 8-column chunks.
-RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int target_wgs, int reverse) {
+// cols_per_thread: 8 (absmax passes) or 16 (pack passes, one block per thread).
+RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int target_wgs, int reverse,
+               int cols_per_thread) {
     RowGeo g;
     g.M = M;
     g.rows_total = rows_total;
     g.ldx = ld;
     g.C8 = (int32_t)(width / 8);
-    g.J = (g.C8 + 1023) / 1024;
-    const int per = (g.C8 + g.J - 1) / g.J;
+    const int chunks = (int)(width / cols_per_thread);
+    g.J = (chunks + 1023) / 1024;
+    const int per = (chunks + g.J - 1) / g.J;
     g.block = (per + 63) / 64 * 64;
-    int64_t rpw = (rows_total + target_wgs - 1) / target_wgs;
-    if (rpw < 1) rpw = 1;
-    g.rows_per_wg = (int32_t)rpw;
-    g.grid = (int32_t)((rows_total + rpw - 1) / rpw);
+    // rows are visited grid-stride; the grid never exceeds the row count
+    const int64_t grid = rows_total < target_wgs ? rows_total : target_wgs;
+    g.grid = (int32_t)(grid > 0 ? grid : 1);
+    g.rows_per_wg = (int32_t)((rows_total + g.grid - 1) / g.grid);
     g.reverse = reverse;
     return g;
 }
 
-constexpr int kTargetWgs = 1024;
+// Grid sizes (rows are visited grid-stride).  The absmax passes end with one
+// atomic per workgroup, so fewer, wider workgroups are best there.
+constexpr int kAbsmaxWgs = 256;
+constexpr int kPackWgs = 1024;
 
 nvfp4_status check_segments(const nvfp4_segments* seg, int64_t M, int64_t D, SegParams* out) {
     if (!seg || !seg->row_start || !seg->shift || !seg->scale) return NVFP4_ERR_INVALID_ARGUMENT;
@@ -105,7 +111,7 @@ nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int6
     if ((st = check_segments(seg, M, D, &sp)) != NVFP4_OK) return st;
     if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
-    const RowGeo g = row_geo(M, M, D, ldx, kTargetWgs, 0);
+    const RowGeo g = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
     return hip_status(launch_modulate_absmax(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out,
                                              (hipStream_t)stream));
 }
@@ -120,7 +126,7 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
     if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
-    const RowGeo g = row_geo(M, M_pad, D, ldx, kTargetWgs, 1);
+    const RowGeo g = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
     return hip_status(launch_modulate_pack(x, g, sp, tensor_scale, qdata, sfa, (hipStream_t)stream));
 }
 
@@ -131,7 +137,7 @@ nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64
     if ((st = check_rows(up, M, F, ld)) != NVFP4_OK) return st;
     if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
-    const RowGeo g = row_geo(M, M, F, ld, kTargetWgs, 0);
+    const RowGeo g = row_geo(M, M, F, ld, kAbsmaxWgs, 0, 8);
     return hip_status(launch_swiglu_absmax(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out,
                                            (hipStream_t)stream));
 }
@@ -145,7 +151,7 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
     if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
-    const RowGeo g = row_geo(M, M_pad, F, ld, kTargetWgs, 1);
+    const RowGeo g = row_geo(M, M_pad, F, ld, kPackWgs, 1, 16);
     return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
 }
 

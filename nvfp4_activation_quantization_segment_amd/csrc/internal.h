@@ -18,14 +18,14 @@ struct SegParams {
 };
 
 // Row-pass geometry: each thread owns 8-column chunks c = threadIdx.x + j*block
-// (j < J) of rows [blockIdx*rows_per_wg, +rows_per_wg).
+// (j < J); workgroup b visits rows b, b+grid, b+2*grid, ... (grid-stride).
 struct RowGeo {
     int64_t M;            // logical rows
     int64_t rows_total;   // rows the grid covers (M, or M_pad when padding is written)
     int64_t ldx;          // input row stride (elements)
     int32_t C8;           // 8-column chunks per row
     int32_t J;            // chunks per thread
-    int32_t rows_per_wg;
+    int32_t rows_per_wg;  // ceil(rows_total / grid), informational
     int32_t grid;
     int32_t block;
     int32_t reverse;      // pack pass walks row tiles last-to-first

@@ -51,14 +51,45 @@ __device__ __forceinline__ uint32_t modulate2(uint32_t x2, float s1a, float s1b,
 
 // ---------------------------------------------------------------------------
 // SwiGLU: h = bf16(bf16(silu(g)) * u), silu(g) = g / (1 + exp(-g)) with a
-// correctly rounded binary32 exp.  The binary64 exp rounded to binary32 is
-// the correctly rounded value for every bf16 g (the exact value is never
-// within the binary64 error of a binary32 rounding midpoint).
+// correctly rounded binary32 exp, every step rounded to binary32, the quotient
+// rounded to bf16.
+//
+// Exact path: the binary64 exp rounded to binary32 is the correctly rounded
+// value for every bf16 g (the exact value is never within the binary64 error
+// of a binary32 rounding midpoint); the rest follows the definition.
+//
+// Fast path (binary32 only): exp(-g) = 2^(a + b) with -g*log2(e) split so that
+// a = -g * L2E_HI is exact (g has 8 significant bits, L2E_HI 15) and b is the
+// small remainder; 2^(a - rint(a) + b) by v_exp_f32, scaled by 2^rint(a).
+// The quotient uses v_rcp_f32 and one fma correction.  The result is within a
+// few binary32 ulps of the exact chain, so it rounds to the same bf16 unless
+// it lies within 16 ulps of a bf16 rounding midpoint; those values (and an
+// overflowing exp) take the exact path.  Because g is bf16, the 65,536 inputs
+// are checked exhaustively against the oracle.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_bf16_value(float g) {
+constexpr float kL2eHi = 0x1.715400p+0f;   // log2(e) to 15 significant bits
+constexpr float kL2eLo = 0x1.d94ae0p-18f;  // log2(e) - kL2eHi, rounded
+
+__device__ __forceinline__ float silu_exact(float g) {
     float e = (float)exp(-(double)g);
     float den = 1.0f + e;
-    float sl = g / den;  // correctly rounded division
+    return g / den;  // correctly rounded division
+}
+
+__device__ __forceinline__ float silu_bf16_value(float g) {
+    float a = -g * kL2eHi;
+    const float b = -g * kL2eLo;
+    a = __builtin_fminf(__builtin_fmaxf(a, -160.0f), 130.0f);
+    const float n = __builtin_rintf(a);
+    const float f = (a - n) + b;
+    const float e = __builtin_ldexpf(__builtin_amdgcn_exp2f(f), (int)n);
+    const float den = 1.0f + e;
+    const float r = __builtin_amdgcn_rcpf(den);
+    const float q0 = g * r;
+    const float e1 = __builtin_fmaf(q0, den, -g);  // residual form keeps the sign of g = -0
+    float sl = __builtin_fmaf(-e1, r, q0);
+    const uint32_t lo = __float_as_uint(sl) & 0xFFFFu;
+    if ((lo - 0x7FF0u) <= 0x20u || !(den < 1e38f)) sl = silu_exact(g);
     return bf16_lo(pack_bf16x2(sl, sl));
 }
 
@@ -72,28 +103,17 @@ __device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2) {
 // E4M3FN (bias 7, max 448, 0x7F = NaN)
 // ---------------------------------------------------------------------------
 // Non-negative t -> nearest E4M3 code, ties to even; t >= 448 -> 0x7E;
-// NaN -> 0x7F.  Normals round the binary32 mantissa to 3 bits in integer
-// arithmetic; below 2^-6 the code is the integer nearest t * 2^9 (the E4M3
-// subnormal step), formed by adding 2^23 in binary32.
+// NaN -> 0x7F.  On gfx950 v_cvt_pk_fp8_f32 converts to OCP E4M3FN with
+// round-to-nearest-even (checked against the oracle on structured covers of
+// every rounding case below 464); saturation and NaN are made explicit.
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-    uint32_t u = __float_as_uint(t);
-    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-    uint32_t code_n = (r >> 20) - (120u << 3);
-    float s = t * 512.0f;
-    s = s + 8388608.0f;
-    uint32_t code_s = __float_as_uint(s) - 0x4B000000u;
-    uint32_t code = (t < 0.015625f) ? code_s : code_n;
-    code = (t >= 448.0f) ? 0x7Eu : code;
-    code = ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7Fu : code;
-    return code;
+    const float tc = t < 448.0f ? t : 448.0f;
+    uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tc, 0.0f, 0, false) & 0xFFu;
+    return (t != t) ? 0x7Fu : code;
 }
 
-// E4M3 code (0..0x7E) -> its binary32 value (exact).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    float vn = __uint_as_float(((c & 0x7Fu) << 20) + (120u << 23));
-    float vs = (float)(c & 7u) * 0.001953125f;
-    return (c & 0x78u) ? vn : vs;
-}
+// E4M3 code -> its binary32 value (exact; v_cvt_f32_fp8 decodes OCP E4M3FN).
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // ---------------------------------------------------------------------------
 // Division by a block constant.

@@ -7,13 +7,13 @@
 // reduce |y| without writing y; read it again and write QDATA/SFA into
 // caller-owned buffers).
 //
-// Layout of the work: one thread owns one 8-column chunk (16 bytes of bf16)
-// of every row in its workgroup's row range.  A workgroup spans every chunk of
-// a row (blockDim = chunks per row rounded up to 64, a thread taking several
-// chunks when a row has more than 1024), so each row is read with contiguous
-// 16-byte loads and the per-column shift/scale stay in registers for the whole
-// row range.  Two neighbouring lanes hold one 16-value block; they exchange
-// their partial maxima with one DPP move.
+// Layout of the work: in pass 1 one thread owns one 8-column chunk (16 bytes
+// of bf16), in pass 2 one 16-column block (32 bytes), of every row its
+// workgroup visits.  A workgroup spans every chunk of a row (blockDim = chunks
+// per row rounded up to 64, a thread taking several chunks when a row has more
+// than 1024), so each row is read with contiguous 16-byte loads and the
+// per-column bf16(scale+1) and shift stay in registers.  Workgroups take rows
+// grid-stride, so the rows in flight form one compact window of the tensor.
 #include "nvfp4_device.h"
 #include "internal.h"
 
@@ -35,14 +35,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// Maximum of the partner lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ uint32_t partner_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+// Workgroup maximum of a 16-bit magnitude, then the grid-level finish: one
+// atomic max per workgroup; the last workgroup to take a ticket turns the
+// maximum into the tensor scale and returns the workspace to zero.
+//
+// Only atomic read-modify-writes touch the two workspace words, and device-
+// scope RMWs on one location are totally ordered, so no cache-wide fence is
+// needed (an agent-scope fence here writes back and invalidates the XCD's L2
+// once per workgroup, which dominated the pass).  Each workgroup consumes the
+// value returned by its max before taking its ticket, so the max has been
+// performed first; the last workgroup reads the maximum with an RMW after
+// every other ticket, hence after every other max.
+__device__ __forceinline__ uint32_t atomic_max_dev(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup maximum of a 16-bit magnitude, then the grid-level finish: one
-// atomic max per workgroup; the last workgroup to arrive turns the maximum
-// into the tensor scale and returns the workspace to zero.
 __device__ void reduce_and_finish(uint32_t m16, uint32_t* ws, float* tensor_scale, float* amax_out) {
     __shared__ uint32_t red[16];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -53,39 +63,36 @@ __device__ void reduce_and_finish(uint32_t m16, uint32_t* ws, float* tensor_scal
         uint32_t mm = 0;
         const int nw = (blockDim.x + 63) >> 6;
         for (int i = 0; i < nw; ++i) mm = red[i] > mm ? red[i] : mm;
-        atomicMax(&ws[0], mm);
-        __threadfence();
-        const uint32_t ticket = atomicAdd(&ws[1], 1u);
+        const uint32_t prev = atomic_max_dev(&ws[0], mm);
+        asm volatile("" ::"v"(prev) : "memory");  // the max is performed before the ticket
+        const uint32_t ticket = atomic_add_dev(&ws[1], 1u);
         if (ticket == gridDim.x - 1) {
-            __threadfence();
-            const uint32_t bits = atomicMax(&ws[0], 0u);
+            const uint32_t bits = atomic_max_dev(&ws[0], 0u);
             const float amax = __uint_as_float(bits << 16);
             // s_g = amax / (6 * 448), or 1 when the tensor is all zero
             const float sg = (amax == 0.0f) ? 1.0f : amax / 2688.0f;
             tensor_scale[0] = sg;
             if (amax_out) amax_out[0] = amax;
-            atomicExch(&ws[0], 0u);
-            atomicExch(&ws[1], 0u);
+            __hip_atomic_exchange(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_exchange(&ws[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-// Per-lane block setup shared by the pack kernels: the block maximum is the
-// max of this lane's 8 magnitudes and its partner's.
-__device__ __forceinline__ void pack_block_store(const uint32_t y[4], float s_g, float rg, bool sg_fast,
-                                                 uint8_t* __restrict__ qrow, uint8_t* __restrict__ srow,
-                                                 int c) {
+// One thread, one whole 16-value block: maximum, scale, codes, and the 8
+// QDATA bytes plus the scale byte stored for block b of a row.
+__device__ __forceinline__ void pack_block16_store(const uint32_t y[8], float s_g, float rg, bool sg_fast,
+                                                   uint8_t* __restrict__ qrow, uint8_t* __restrict__ srow,
+                                                   int b) {
     uint32_t m2 = mag2(y[0]);
-    m2 = pk_max_u16(m2, mag2(y[1]));
-    m2 = pk_max_u16(m2, mag2(y[2]));
-    m2 = pk_max_u16(m2, mag2(y[3]));
-    uint32_t m = fold_max(m2);
-    const uint32_t p = partner_u32(m);
-    m = m > p ? m : p;
-    const BlockQ b = block_setup(m, s_g, rg, sg_fast);
-    const uint32_t w = quantize8(y, b.d, b.r, b.fast) & b.keep;
-    *reinterpret_cast<uint32_t*>(qrow + 4 * c) = w;
-    if ((c & 1) == 0) srow[c >> 1] = (uint8_t)b.sf;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
+    const BlockQ bq = block_setup(fold_max(m2), s_g, rg, sg_fast);
+    uint2 w;
+    w.x = quantize8(y, bq.d, bq.r, bq.fast) & bq.keep;
+    w.y = quantize8(y + 4, bq.d, bq.r, bq.fast) & bq.keep;
+    *reinterpret_cast<uint2*>(qrow + 8 * b) = w;
+    srow[b] = (uint8_t)bq.sf;
 }
 
 // ---------------------------------------------------------------------------
@@ -117,48 +124,64 @@ __device__ __forceinline__ void modulate8(const uint4 xv, const ColParams& cp, u
     y[3] = modulate2(xv.w, cp.s1[6], cp.s1[7], cp.sh[6], cp.sh[7]);
 }
 
+// Segment of row r: segments are contiguous row ranges; rows visit in order,
+// so the caller keeps the current segment and its end and advances rarely.
+__device__ __forceinline__ int seg_advance(const SegParams& seg, int64_t r, int s) {
+    while (r >= seg.row_start[s + 1]) ++s;
+    return s;
+}
+
+// Rows are assigned grid-stride (workgroup b takes rows b, b+G, b+2G, ...), so
+// the workgroups resident at any moment read one compact window of the tensor
+// that sweeps through it, which is what the memory system streams best.
 __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                                SegParams seg, uint32_t* ws,
                                                                float* tensor_scale, float* amax_out) {
-    const int64_t r0 = (int64_t)blockIdx.x * g.rows_per_wg;
-    const int64_t r1 = r0 + g.rows_per_wg < g.M ? r0 + g.rows_per_wg : g.M;
+    const int64_t G = gridDim.x;
     uint32_t m2 = 0;
     for (int j = 0; j < g.J; ++j) {
         const int c = threadIdx.x + j * blockDim.x;
         if (c >= g.C8) break;
-        for (int s = 0; s < seg.count; ++s) {
-            const int64_t a = r0 > seg.row_start[s] ? r0 : seg.row_start[s];
-            const int64_t b = r1 < seg.row_start[s + 1] ? r1 : seg.row_start[s + 1];
-            if (a >= b) continue;
-            ColParams cp;
-            load_cols(seg, s, c, cp);
-            const uint16_t* xp = x + a * g.ldx + 8 * c;
-            int64_t r = a;
-            for (; r + 4 <= b; r += 4) {
-                uint4 v[4];
+        int64_t r = blockIdx.x;
+        int s = seg_advance(seg, r < g.M ? r : 0, 0);
+        ColParams cp;
+        load_cols(seg, s, c, cp);
+        for (; r + 3 * G < g.M; r += 4 * G) {
+            uint4 v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v[u] = ld16(xp + u * g.ldx);
+            for (int u = 0; u < 4; ++u) v[u] = ld16(x + (r + u * G) * g.ldx + 8 * c);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uint32_t y[4];
-                    modulate8(v[u], cp, y);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
+            for (int u = 0; u < 4; ++u) {
+                const int su = seg_advance(seg, r + u * G, s);
+                if (su != s) {
+                    s = su;
+                    load_cols(seg, s, c, cp);
                 }
-                xp += 4 * g.ldx;
-            }
-            for (; r < b; ++r) {
                 uint32_t y[4];
-                modulate8(ld16(xp), cp, y);
+                modulate8(v[u], cp, y);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
-                xp += g.ldx;
             }
+        }
+        for (; r < g.M; r += G) {
+            const int su = seg_advance(seg, r, s);
+            if (su != s) {
+                s = su;
+                load_cols(seg, s, c, cp);
+            }
+            uint32_t y[4];
+            modulate8(ld16(x + r * g.ldx + 8 * c), cp, y);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
         }
     }
     reduce_and_finish(fold_max(m2), ws, tensor_scale, amax_out);
 }
 
+// Pass 2: one thread per 16-value block (two 16-byte loads per row), so the
+// block scale is computed once.  Rows are walked last-to-first (grid-stride
+// from the end), so the rows pass 1 read last, which are still in the
+// memory-side cache, are read first.
 __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                              SegParams seg, const float* tensor_scale,
                                                              uint8_t* __restrict__ qdata,
@@ -166,42 +189,39 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
     const float s_g = tensor_scale[0];
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
-    const int64_t tile = reverse ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
-    const int64_t r0 = tile * g.rows_per_wg;
-    const int64_t r1 = r0 + g.rows_per_wg < g.rows_total ? r0 + g.rows_per_wg : g.rows_total;
-    const int64_t qld = 4 * (int64_t)g.C8, sld = g.C8 >> 1;
+    const int64_t G = gridDim.x;
+    const int C16 = g.C8 >> 1;
+    const int64_t qld = 8 * (int64_t)C16, sld = C16;
     for (int j = 0; j < g.J; ++j) {
-        const int c = threadIdx.x + j * blockDim.x;
-        if (c >= g.C8) break;
-        const int64_t rm = r1 < g.M ? r1 : g.M;
-        for (int s = 0; s < seg.count; ++s) {
-            const int64_t a = r0 > seg.row_start[s] ? r0 : seg.row_start[s];
-            const int64_t b = rm < seg.row_start[s + 1] ? rm : seg.row_start[s + 1];
-            if (a >= b) continue;
-            ColParams cp;
-            load_cols(seg, s, c, cp);
-            const uint16_t* xp = x + a * g.ldx + 8 * c;
-            int64_t r = a;
-            for (; r + 2 <= b; r += 2) {
-                const uint4 v0 = ld16(xp), v1 = ld16(xp + g.ldx);
-                uint32_t y[4];
-                modulate8(v0, cp, y);
-                pack_block_store(y, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, c);
-                modulate8(v1, cp, y);
-                pack_block_store(y, s_g, rg, sg_fast, qdata + (r + 1) * qld, sfa + (r + 1) * sld, c);
-                xp += 2 * g.ldx;
-            }
-            for (; r < b; ++r) {
-                uint32_t y[4];
-                modulate8(ld16(xp), cp, y);
-                pack_block_store(y, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, c);
-                xp += g.ldx;
-            }
+        const int b = threadIdx.x + j * blockDim.x;
+        if (b >= C16) break;
+        // padding rows M .. rows_total-1 are zero
+        for (int64_t r = g.M + blockIdx.x; r < g.rows_total; r += G) {
+            *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
+            sfa[r * sld + b] = 0;
         }
-        // zero padding rows M .. rows_total-1
-        for (int64_t r = (r0 > g.M ? r0 : g.M); r < r1; ++r) {
-            *reinterpret_cast<uint32_t*>(qdata + r * qld + 4 * c) = 0u;
-            if ((c & 1) == 0) sfa[r * sld + (c >> 1)] = 0;
+        int64_t i = blockIdx.x;
+        if (i >= g.M) continue;
+        int64_t r = reverse ? g.M - 1 - i : i;
+        int s = 0;
+        while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
+        ColParams cp0, cp1;
+        load_cols(seg, s, 2 * b, cp0);
+        load_cols(seg, s, 2 * b + 1, cp1);
+        for (; i < g.M; i += G) {
+            r = reverse ? g.M - 1 - i : i;
+            const uint16_t* xp = x + r * g.ldx + 16 * b;
+            const uint4 v0 = ld16(xp), v1 = ld16(xp + 8);
+            if (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) {
+                s = 0;
+                while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
+                load_cols(seg, s, 2 * b, cp0);
+                load_cols(seg, s, 2 * b + 1, cp1);
+            }
+            uint32_t y[8];
+            modulate8(v0, cp0, y);
+            modulate8(v1, cp1, y + 4);
+            pack_block16_store(y, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, b);
         }
     }
 }
@@ -220,21 +240,28 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ up, RowGeo g,
                                                              uint32_t* ws, float* tensor_scale,
                                                              float* amax_out) {
-    const int64_t r0 = (int64_t)blockIdx.x * g.rows_per_wg;
-    const int64_t r1 = r0 + g.rows_per_wg < g.M ? r0 + g.rows_per_wg : g.M;
+    const int64_t G = gridDim.x;
     uint32_t m2 = 0;
     for (int j = 0; j < g.J; ++j) {
         const int c = threadIdx.x + j * blockDim.x;
         if (c >= g.C8) break;
-        const uint16_t* gp = gate + r0 * g.ldx + 8 * c;
-        const uint16_t* upp = up + r0 * g.ldx + 8 * c;
-        for (int64_t r = r0; r < r1; ++r) {
+        int64_t r = blockIdx.x;
+        for (; r + G < g.M; r += 2 * G) {
+            const uint4 g0 = ld16(gate + r * g.ldx + 8 * c), u0 = ld16(up + r * g.ldx + 8 * c);
+            const uint4 g1 = ld16(gate + (r + G) * g.ldx + 8 * c), u1 = ld16(up + (r + G) * g.ldx + 8 * c);
             uint32_t h[4];
-            swiglu8(ld16(gp), ld16(upp), h);
+            swiglu8(g0, u0, h);
 #pragma unroll
             for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
-            gp += g.ldx;
-            upp += g.ldx;
+            swiglu8(g1, u1, h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
+        }
+        for (; r < g.M; r += G) {
+            uint32_t h[4];
+            swiglu8(ld16(gate + r * g.ldx + 8 * c), ld16(up + r * g.ldx + 8 * c), h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
         }
     }
     reduce_and_finish(fold_max(m2), ws, tensor_scale, amax_out);
@@ -248,26 +275,24 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
     const float s_g = tensor_scale[0];
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
-    const int64_t tile = reverse ? (int64_t)(gridDim.x - 1 - blockIdx.x) : (int64_t)blockIdx.x;
-    const int64_t r0 = tile * g.rows_per_wg;
-    const int64_t r1 = r0 + g.rows_per_wg < g.rows_total ? r0 + g.rows_per_wg : g.rows_total;
-    const int64_t qld = 4 * (int64_t)g.C8, sld = g.C8 >> 1;
+    const int64_t G = gridDim.x;
+    const int C16 = g.C8 >> 1;
+    const int64_t qld = 8 * (int64_t)C16, sld = C16;
     for (int j = 0; j < g.J; ++j) {
-        const int c = threadIdx.x + j * blockDim.x;
-        if (c >= g.C8) break;
-        const int64_t rm = r1 < g.M ? r1 : g.M;
-        const uint16_t* gp = gate + r0 * g.ldx + 8 * c;
-        const uint16_t* upp = up + r0 * g.ldx + 8 * c;
-        for (int64_t r = r0; r < rm; ++r) {
-            uint32_t h[4];
-            swiglu8(ld16(gp), ld16(upp), h);
-            pack_block_store(h, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, c);
-            gp += g.ldx;
-            upp += g.ldx;
+        const int b = threadIdx.x + j * blockDim.x;
+        if (b >= C16) break;
+        for (int64_t r = g.M + blockIdx.x; r < g.rows_total; r += G) {
+            *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
+            sfa[r * sld + b] = 0;
         }
-        for (int64_t r = (r0 > g.M ? r0 : g.M); r < r1; ++r) {
-            *reinterpret_cast<uint32_t*>(qdata + r * qld + 4 * c) = 0u;
-            if ((c & 1) == 0) sfa[r * sld + (c >> 1)] = 0;
+        for (int64_t i = blockIdx.x; i < g.M; i += G) {
+            const int64_t r = reverse ? g.M - 1 - i : i;
+            const uint16_t* gp = gate + r * g.ldx + 16 * b;
+            const uint16_t* upp = up + r * g.ldx + 16 * b;
+            uint32_t h[8];
+            swiglu8(ld16(gp), ld16(upp), h);
+            swiglu8(ld16(gp + 8), ld16(upp + 8), h + 4);
+            pack_block16_store(h, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, b);
         }
     }
 }

@@ -35,6 +35,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="before timing, copy 1 GiB once (a plain copy kernel of known size, for scaling "
+                        "rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     return p.parse_args()
 
 
@@ -152,6 +155,15 @@ def main():
 
     seq = launches()
     n = len(seq)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            src.fill_(1)
+            dst.copy_(src)
+        stream.synchronize()
+        del src, dst
 
     def run_step(events=None):
         for i, (_, _, fn) in enumerate(seq):

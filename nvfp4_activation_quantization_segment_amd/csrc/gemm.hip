@@ -17,15 +17,20 @@
 // Tiling.  A workgroup of 8 waves (two per SIMD) computes a 256x256 output
 // tile; each wave a 128(M) x 64(N) sub-tile as 4x2 v_mfma_f32_32x32x16_f16
 // tiles with 128 fp32 accumulators per lane.  Every packed element is decoded
-// once per workgroup: thread t < 256 decodes activation row t, thread t >= 256
-// weight row t-256, 64 values per K step of 64, into double-buffered fp16
-// tiles in LDS (256 rows x 64, row stride 144 bytes so that the 32 rows one
-// MFMA fragment reads fall on distinct bank groups); the waves then read their
-// fragments with 16-byte LDS loads.  The MFMA A operand is the weight (rows
-// n) and the B operand the activation (rows m), so each lane's accumulators
-// hold four consecutive n of one m and the epilogue stores 8 contiguous bytes.
-// Two waves per SIMD let the hardware overlap one wave's decode and LDS work
-// with the other's MFMAs.
+// once per workgroup into double-buffered fp16 tiles in LDS (256 rows x 64 per
+// operand, row stride 144 bytes so that the 32 rows one MFMA fragment reads
+// fall on distinct bank groups); the waves then read their fragments with
+// 16-byte LDS loads.  The MFMA A operand is the weight (rows n) and the B
+// operand the activation (rows m), so each lane's accumulators hold four
+// consecutive n of one m and the epilogue stores 8 contiguous bytes.
+//
+// Global loads.  Waves 0-3 stage activation rows and waves 4-7 weight rows, 64
+// rows per wave.  Lanes 2r and 2r+1 load the two 16-byte halves of one row's
+// 32-byte K step, so a load instruction touches 32 rows rather than 64, and
+// block scales are fetched for four K steps at a time (16 bytes per row).
+// Measured on the projection shapes this halves the L1 accesses and L2
+// requests of a one-row-per-lane layout, whose vector memory path was close to
+// saturation; the energy saved shows up as clock under the power limit.
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -63,59 +68,93 @@ constexpr int kLDK = kBK + 8;
 constexpr int kTileHalves = kBM * kLDK;  // per operand per stage
 constexpr int kLdsBytes = 2 /*stages*/ * 2 /*operands*/ * kTileHalves * 2;
 
+// One K step of the thread's two half rows: 32 nibbles each.
 struct RowPack {
-    uint4 q0, q1;  // 64 nibbles of one row for one K step
-    uint32_t sc;   // its 4 block scales
+    uint4 q[2];
+};
+// Block scales of the thread's two rows for a group of 4 K steps: word j of
+// s[i] holds the 4 scales of row i in step 4g+j.
+struct ScaleGrp {
+    uint4 s[2];
 };
 
-__device__ __forceinline__ RowPack load_row(const uint8_t* q, const uint8_t* sf, uint32_t qoff, uint32_t soff) {
+__device__ __forceinline__ RowPack load_row(const uint8_t* q, uint32_t q0, uint32_t q1) {
     RowPack r;
-    r.q0 = *reinterpret_cast<const uint4*>(q + qoff);
-    r.q1 = *reinterpret_cast<const uint4*>(q + qoff + 16);
-    r.sc = *reinterpret_cast<const uint32_t*>(sf + soff);
+    r.q[0] = *reinterpret_cast<const uint4*>(q + q0);
+    r.q[1] = *reinterpret_cast<const uint4*>(q + q1);
     return r;
 }
 
-// Decode one row's 64 values into LDS (8 x 16-byte stores).
-__device__ __forceinline__ void store_row(const RowPack& r, _Float16* dst) {
+// Scales of group g.  With SC4 (scale rows and base pointers 16-byte aligned,
+// K a multiple of 256) one 16-byte load per row; otherwise four 4-byte loads,
+// steps past the last clamped to it.
+template <bool SC4>
+__device__ __forceinline__ ScaleGrp load_grp(const uint8_t* sf, uint32_t s0, uint32_t s1, int g, int nit) {
+    ScaleGrp r;
+    if (SC4) {
+        r.s[0] = *reinterpret_cast<const uint4*>(sf + s0 + 16u * g);
+        r.s[1] = *reinterpret_cast<const uint4*>(sf + s1 + 16u * g);
+    } else {
+        uint32_t w[2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t w = word_of(i < 4 ? r.q0 : r.q1, i & 3);
-        const f16x8 v = decode8(w, sf_raw2(r.sc, i >> 1));
-        *reinterpret_cast<f16x8*>(dst + 8 * i) = v;
+        for (int j = 0; j < 4; ++j) {
+            const int st = 4 * g + j < nit ? 4 * g + j : nit - 1;
+            w[0][j] = *reinterpret_cast<const uint32_t*>(sf + s0 + 4u * st);
+            w[1][j] = *reinterpret_cast<const uint32_t*>(sf + s1 + 4u * st);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) r.s[i] = (uint4){w[i][0], w[i][1], w[i][2], w[i][3]};
     }
+    return r;
 }
 
-// Decode words 2p and 2p+1 of a staged row (the 16 values of block p) into
-// LDS: two 16-byte stores.
-__device__ __forceinline__ void store_part(const RowPack& r, int p, _Float16* dst) {
+// Decode part p (row p>>1, words 2(p&1) and 2(p&1)+1: the 16 values of one
+// block) of the thread's staged half rows into LDS: two 16-byte stores.  sc[i]
+// is row i's scale word of the step; hb = 2h indexes the first scale byte of
+// this thread's half row.
+__device__ __forceinline__ void store_part(const RowPack& r, const uint32_t (&sc)[2], int p, _Float16* dst0,
+                                           _Float16* dst1, int hb) {
+    const int i = p >> 1, wp = p & 1;
+    const uint32_t s2 = sf_raw2(sc[i], hb + wp);
+    _Float16* dst = i == 0 ? dst0 : dst1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int i = 2 * p + u;
-        const uint32_t w = word_of(i < 4 ? r.q0 : r.q1, i & 3);
-        *reinterpret_cast<f16x8*>(dst + 8 * i) = decode8(w, sf_raw2(r.sc, i >> 1));
+        const int w = 2 * wp + u;
+        *reinterpret_cast<f16x8*>(dst + 8 * w) = decode8(word_of(r.q[i], w), s2);
     }
 }
 
-// One K step on LDS buffer CUR, in four phases (one per 16-wide K slice j):
-// read the fragments of slice j+1, decode a quarter of this thread's row of the
-// next stage (DECODE) into the other buffer, and issue the 8 MFMAs of slice j.
-// CUR is a template parameter so that both buffers' offsets are constants and
-// the reads of one buffer and the writes of the other are visibly independent.
-// The packed row of the stage after next is fetched at the start of the step.
-template <int CUR, bool DECODE>
+// Per-thread staging geometry.
+struct Stage {
+    const uint8_t* q;   // packed rows of the thread's operand
+    const uint8_t* sf;  // their scales
+    uint32_t q0, q1;    // byte offsets of the two half rows (step 0)
+    uint32_t s0, s1;    // byte offsets of the two scale rows
+    int dop;            // LDS operand index: 0 activation, 2 weight
+    int d0, d1;         // LDS offsets (halves) of the two decoded half rows
+    int hb;             // 2 * (half of the row this thread holds)
+};
+
+// K step `it` on LDS buffer CUR, in four phases (one per 16-wide K slice j):
+// read the fragments of slice j+1, decode one part of this thread's share of
+// step it+1 into the other buffer, and issue the 8 MFMAs of slice j.  CUR is a
+// template parameter so that both buffers' offsets are constants and the reads
+// of one buffer and the writes of the other are visibly independent.  The
+// packed data of step it+2 (and, with LOADG, the scale group after the current
+// one) is fetched at the start of the step.  SW selects the scale word of step
+// it+1: word SW of the current group, or word 0 of the next group for SW == 4.
+template <int CUR, int SW, bool LOADG, bool SC4>
 __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)[2][4], RowPack& ra,
-                                       const GemmArgs& a, uint32_t roff, uint32_t rso, const uint8_t* q,
-                                       const uint8_t* sf, int next_stage, int tid, int wrow0, int arow0, int h) {
+                                       ScaleGrp& gc, ScaleGrp& gn, const Stage& st, int next_stage,
+                                       int next_grp, int nit, int wrow0, int arow0, int h) {
     const _Float16* cA = lds + CUR * kTileHalves;
     const _Float16* cW = lds + (2 + CUR) * kTileHalves;
-    // thread tid < 256 decodes activation row tid, else weight row tid-256
-    _Float16* dst = lds + ((tid < 256 ? 0 : 2) + (CUR ^ 1)) * kTileHalves + (tid & 255) * kLDK;
-    RowPack na;
-    if (DECODE) {
-        const uint32_t db = 32u * next_stage, ds = 4u * next_stage;
-        na = load_row(q, sf, roff + db, rso + ds);
-    }
+    _Float16* dst0 = lds + (st.dop + (CUR ^ 1)) * kTileHalves + st.d0;
+    _Float16* dst1 = lds + (st.dop + (CUR ^ 1)) * kTileHalves + st.d1;
+    const ScaleGrp& gs = SW < 4 ? gc : gn;
+    const uint32_t sc[2] = {word_of(gs.s[0], SW & 3), word_of(gs.s[1], SW & 3)};
+    const RowPack na = load_row(st.q, st.q0 + 32u * next_stage, st.q1 + 32u * next_stage);
+    if (LOADG) gn = load_grp<SC4>(st.sf, st.s0, st.s1, next_grp, nit);
     f16x8 wf[2][2], af[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) wf[0][i] = *reinterpret_cast<const f16x8*>(cW + (wrow0 + 32 * i) * kLDK + 8 * h);
@@ -133,7 +172,7 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
             for (int i = 0; i < 4; ++i)
                 af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
         }
-        if (DECODE) store_part(ra, j, dst);
+        store_part(ra, sc, j, dst0, dst1, st.hb);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -141,22 +180,24 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
                 acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[b][i], af[b][k], acc[i][k], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (DECODE) ra = na;
+    ra = na;
+    if (SW == 4) gc = gn;
     __syncthreads();
 }
 
+template <bool SC4>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
 gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
 
     // Tile order: each XCD (workgroups are dealt round-robin over 8) takes a
-    // contiguous range of tiles, walked in groups of 8 M-tiles so that the
+    // contiguous range of tiles, walked in groups of 4 M-tiles so that the
     // workgroups resident on one XCD share activation and weight rows in L2.
     const int T = tiles_m * tiles_n;
     const int bid = blockIdx.x;
     const int per = T / 8;
     const int logical = (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
-    constexpr int GM = 8;
+    constexpr int GM = 4;
     const int gsz = GM * tiles_n;
     const int first_m = (logical / gsz) * GM;
     const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
@@ -168,39 +209,90 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
     const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, l32 = lane & 31;
     const uint32_t Kb = (uint32_t)a.K >> 1, Ks = (uint32_t)a.K >> 4;
-    const uint8_t* q = tid < 256 ? a.qa : a.qw;
-    const uint8_t* sf = tid < 256 ? a.sfa : a.sfw;
-    int row;
-    if (tid < 256) { row = tm * kBM + tid; row = row < a.M_pad ? row : a.M_pad - 1; }
-    else { row = tn * kBN + (tid - 256); row = row < a.N ? row : a.N - 1; }
-    const uint32_t roff = (uint32_t)row * Kb, rso = (uint32_t)row * Ks;
+
+    // Staging role: lane 2r+sh of wave w holds half sh of rows r and r+32 of
+    // the 64 rows (w & 3) * 64 .. of the activation tile (w < 4) or the weight
+    // tile (w >= 4); rows past the end are clamped to the last row.
+    Stage st;
+    const bool is_a = wave < 4;
+    st.q = is_a ? a.qa : a.qw;
+    st.sf = is_a ? a.sfa : a.sfw;
+    const int sh = lane & 1;
+    const int lr = (wave & 3) * 64 + (lane >> 1);
+    {
+        uint32_t qo[2], so[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int row;
+            if (is_a) {
+                row = tm * kBM + lr + 32 * i;
+                row = row < a.M_pad ? row : a.M_pad - 1;
+            } else {
+                row = tn * kBN + lr + 32 * i;
+                row = row < a.N ? row : a.N - 1;
+            }
+            qo[i] = (uint32_t)row * Kb + 16u * sh;
+            so[i] = (uint32_t)row * Ks;
+        }
+        st.q0 = qo[0];
+        st.q1 = qo[1];
+        st.s0 = so[0];
+        st.s1 = so[1];
+    }
+    st.dop = is_a ? 0 : 2;
+    st.d0 = lr * kLDK + 32 * sh;
+    st.d1 = (lr + 32) * kLDK + 32 * sh;
+    st.hb = 2 * sh;
 
     f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[i][k] = (f32x16){0};
-    const int wrow0 = wn * 64 + l32;
-    const int arow0 = wm * 128 + l32;
+    const int wrow0 = wn * kWN + l32;
+    const int arow0 = wm * kWM + l32;
     const int nit = a.K / kBK;
-    RowPack ra = load_row(q, sf, roff, rso);
-    store_row(ra, lds + (tid < 256 ? 0 : 2) * kTileHalves + (tid & 255) * kLDK);
+    const int ngrp = (nit + 3) / 4;
+    const int lastst = nit - 1;
+
+    // Prologue: decode step 0 into buffer 0, fetch step 1.
+    RowPack ra = load_row(st.q, st.q0, st.q1);
+    ScaleGrp gc = load_grp<SC4>(st.sf, st.s0, st.s1, 0, nit), gn = gc;
     {
-        const int s1 = nit > 1 ? 1 : 0;
-        ra = load_row(q, sf, roff + 32u * s1, rso + 4u * s1);
+        const uint32_t sc[2] = {gc.s[0].x, gc.s[1].x};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            store_part(ra, sc, p, lds + st.dop * kTileHalves + st.d0, lds + st.dop * kTileHalves + st.d1, st.hb);
+    }
+    {
+        const uint32_t s1 = nit > 1 ? 1 : 0;
+        ra = load_row(st.q, st.q0 + 32u * s1, st.q1 + 32u * s1);
     }
     __syncthreads();
+
+    // Step it decodes step it+1 (scale word (it+1) % 4) and fetches the data of
+    // step it+2; the step with it % 4 == 2 also fetches the next scale group.
+    // Fetches past the last step are clamped to it and never used.
     int it = 0;
-    for (; it + 2 <= nit - 1; it += 2) {
-        const int n2 = it + 2 < nit ? it + 2 : nit - 1;
-        const int n3 = it + 3 < nit ? it + 3 : nit - 1;
-        k_step<0, true>(lds, acc, ra, a, roff, rso, q, sf, n2, tid, wrow0, arow0, h);
-        k_step<1, true>(lds, acc, ra, a, roff, rso, q, sf, n3, tid, wrow0, arow0, h);
+#define NVFP4_KSTEP(C, SW, LG, NS)                                                                        \
+    k_step<C, SW, LG, SC4>(lds, acc, ra, gc, gn, st, (NS) < lastst ? (NS) : lastst,                      \
+                           (it >> 2) + 1 < ngrp ? (it >> 2) + 1 : ngrp - 1, nit, wrow0, arow0, h)
+    for (; it + 4 <= nit - 1; it += 4) {
+        NVFP4_KSTEP(0, 1, false, it + 2);
+        NVFP4_KSTEP(1, 2, false, it + 3);
+        NVFP4_KSTEP(0, 3, true, it + 4);
+        NVFP4_KSTEP(1, 4, false, it + 5);
     }
-    if (it < nit - 1) {
-        k_step<0, true>(lds, acc, ra, a, roff, rso, q, sf, nit - 1, tid, wrow0, arow0, h);
-        ++it;
+    {
+        const int rem = nit - 1 - it;  // 0..3 decoding steps left, uniform
+        if (rem > 0) NVFP4_KSTEP(0, 1, false, it + 2);
+        if (rem > 1) NVFP4_KSTEP(1, 2, false, it + 3);
+        if (rem > 2) NVFP4_KSTEP(0, 3, true, it + 4);
+        it += rem;
     }
+#undef NVFP4_KSTEP
+
+    // Last step: MFMAs only.
     {
         const _Float16* cA = lds + (it & 1) * kTileHalves;
         const _Float16* cW = lds + (2 + (it & 1)) * kTileHalves;
@@ -246,7 +338,14 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int tiles_m = (a.M + kBM - 1) / kBM;
     const int tiles_n = (a.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL(gemm_kernel, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
+    // 16-byte scale-group loads need every scale row and both base pointers
+    // 16-byte aligned, i.e. K/16 a multiple of 16.
+    const bool sc4 = (a.K >> 4) % 16 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.sfa) | reinterpret_cast<uintptr_t>(a.sfw)) & 15) == 0;
+    if (sc4)
+        hipLaunchKernelGGL(gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL(gemm_kernel<false>, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
     return hipGetLastError();
 }
 

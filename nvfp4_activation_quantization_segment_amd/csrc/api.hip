@@ -45,6 +45,8 @@ RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int tar
 // atomic per workgroup, so fewer, wider workgroups are best there.
 constexpr int kAbsmaxWgs = 256;
 constexpr int kPackWgs = 1024;
+// The SwiGLU passes hold a 128 KB table in LDS: one workgroup per CU.
+constexpr int kSwigluPackWgs = 256;
 
 nvfp4_status check_segments(const nvfp4_segments* seg, int64_t M, int64_t D, SegParams* out) {
     if (!seg || !seg->row_start || !seg->shift || !seg->scale) return NVFP4_ERR_INVALID_ARGUMENT;
@@ -151,7 +153,7 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
     if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
-    const RowGeo g = row_geo(M, M_pad, F, ld, kPackWgs, 1, 16);
+    const RowGeo g = row_geo(M, M_pad, F, ld, kSwigluPackWgs, 1, 16);
     return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
 }
 

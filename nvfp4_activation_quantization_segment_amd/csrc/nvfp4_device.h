@@ -65,7 +65,8 @@ __device__ __forceinline__ uint32_t modulate2(uint32_t x2, float s1a, float s1b,
 // few binary32 ulps of the exact chain, so it rounds to the same bf16 unless
 // it lies within 16 ulps of a bf16 rounding midpoint; those values (and an
 // overflowing exp) take the exact path.  Because g is bf16, the 65,536 inputs
-// are checked exhaustively against the oracle.
+// are checked exhaustively against the oracle.  The producer kernels evaluate
+// this once per bf16 bit pattern into a lookup table at the start of a call.
 // ---------------------------------------------------------------------------
 constexpr float kL2eHi = 0x1.715400p+0f;   // log2(e) to 15 significant bits
 constexpr float kL2eLo = 0x1.d94ae0p-18f;  // log2(e) - kL2eHi, rounded
@@ -91,12 +92,6 @@ __device__ __forceinline__ float silu_bf16_value(float g) {
     const uint32_t lo = __float_as_uint(sl) & 0xFFFFu;
     if ((lo - 0x7FF0u) <= 0x20u || !(den < 1e38f)) sl = silu_exact(g);
     return bf16_lo(pack_bf16x2(sl, sl));
-}
-
-__device__ __forceinline__ uint32_t swiglu2(uint32_t g2, uint32_t u2) {
-    float sa = silu_bf16_value(bf16_lo(g2));
-    float sb = silu_bf16_value(bf16_hi(g2));
-    return pack_bf16x2(sa * bf16_lo(u2), sb * bf16_hi(u2));
 }
 
 // ---------------------------------------------------------------------------

@@ -228,18 +228,55 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
 
 // ---------------------------------------------------------------------------
 // SwiGLU producer
+//
+// g is bf16, so bf16(silu(g)) takes at most 65,536 values.  A fill kernel
+// evaluates silu_bf16_value for every bf16 bit pattern into g_silu_lut at the
+// start of every SwiGLU call (in stream order, so the table is complete before
+// the pass that reads it); each producer workgroup copies the 128 KB table
+// into LDS and the per-element work becomes one LDS lookup, one binary32
+// product with u and one rounding to bf16.  Concurrent calls on other streams
+// rewrite the table with the same values.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void swiglu8(const uint4 gv, const uint4 uv, uint32_t h[4]) {
-    h[0] = swiglu2(gv.x, uv.x);
-    h[1] = swiglu2(gv.y, uv.y);
-    h[2] = swiglu2(gv.z, uv.z);
-    h[3] = swiglu2(gv.w, uv.w);
+__device__ uint16_t g_silu_lut[65536];
+
+__global__ __launch_bounds__(256) void silu_lut_fill_kernel() {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 65536u) {
+        const float sl = silu_bf16_value(__uint_as_float(i << 16));
+        g_silu_lut[i] = (uint16_t)(__float_as_uint(sl) >> 16);
+    }
+}
+
+constexpr int kLutWords = 65536 * 2 / 16;  // uint4 words in the table
+
+__device__ __forceinline__ void lut_to_lds(uint16_t* slut) {
+    const uint4* src = reinterpret_cast<const uint4*>(g_silu_lut);
+    uint4* dst = reinterpret_cast<uint4*>(slut);
+    for (int i = threadIdx.x; i < kLutWords; i += blockDim.x) dst[i] = src[i];
+    __syncthreads();
+}
+
+// h = bf16(bf16(silu(g)) * u) for two packed bf16 pairs; bf16(silu(g)) from
+// the table (the product of two bf16 values is exact in binary32).
+__device__ __forceinline__ uint32_t swiglu2_lut(const uint16_t* lut, uint32_t g2, uint32_t u2) {
+    const float sa = __uint_as_float((uint32_t)lut[g2 & 0xFFFFu] << 16);
+    const float sb = __uint_as_float((uint32_t)lut[g2 >> 16] << 16);
+    return pack_bf16x2(sa * bf16_lo(u2), sb * bf16_hi(u2));
+}
+
+__device__ __forceinline__ void swiglu8(const uint16_t* lut, const uint4 gv, const uint4 uv, uint32_t h[4]) {
+    h[0] = swiglu2_lut(lut, gv.x, uv.x);
+    h[1] = swiglu2_lut(lut, gv.y, uv.y);
+    h[2] = swiglu2_lut(lut, gv.z, uv.z);
+    h[3] = swiglu2_lut(lut, gv.w, uv.w);
 }
 
 __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __restrict__ gate,
                                                              const uint16_t* __restrict__ up, RowGeo g,
                                                              uint32_t* ws, float* tensor_scale,
                                                              float* amax_out) {
+    __shared__ __attribute__((aligned(16))) uint16_t slut[65536];
+    lut_to_lds(slut);
     const int64_t G = gridDim.x;
     uint32_t m2 = 0;
     for (int j = 0; j < g.J; ++j) {
@@ -250,16 +287,16 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
             const uint4 g0 = ld16(gate + r * g.ldx + 8 * c), u0 = ld16(up + r * g.ldx + 8 * c);
             const uint4 g1 = ld16(gate + (r + G) * g.ldx + 8 * c), u1 = ld16(up + (r + G) * g.ldx + 8 * c);
             uint32_t h[4];
-            swiglu8(g0, u0, h);
+            swiglu8(slut, g0, u0, h);
 #pragma unroll
             for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
-            swiglu8(g1, u1, h);
+            swiglu8(slut, g1, u1, h);
 #pragma unroll
             for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
         }
         for (; r < g.M; r += G) {
             uint32_t h[4];
-            swiglu8(ld16(gate + r * g.ldx + 8 * c), ld16(up + r * g.ldx + 8 * c), h);
+            swiglu8(slut, ld16(gate + r * g.ldx + 8 * c), ld16(up + r * g.ldx + 8 * c), h);
 #pragma unroll
             for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(h[k]));
         }
@@ -272,6 +309,8 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
                                                            const float* tensor_scale,
                                                            uint8_t* __restrict__ qdata,
                                                            uint8_t* __restrict__ sfa, int reverse) {
+    __shared__ __attribute__((aligned(16))) uint16_t slut[65536];
+    lut_to_lds(slut);
     const float s_g = tensor_scale[0];
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
@@ -290,8 +329,8 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
             const uint16_t* gp = gate + r * g.ldx + 16 * b;
             const uint16_t* upp = up + r * g.ldx + 16 * b;
             uint32_t h[8];
-            swiglu8(ld16(gp), ld16(upp), h);
-            swiglu8(ld16(gp + 8), ld16(upp + 8), h + 4);
+            swiglu8(slut, ld16(gp), ld16(upp), h);
+            swiglu8(slut, ld16(gp + 8), ld16(upp + 8), h + 4);
             pack_block16_store(h, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, b);
         }
     }
@@ -309,9 +348,11 @@ __global__ void step_modulate_kernel(const uint16_t* x, const uint16_t* sc, cons
     }
 }
 
+// Reads the same table as the producer (from global memory), so that checking
+// this step over all inputs checks every table entry the producer can use.
 __global__ void step_swiglu_kernel(const uint16_t* g, const uint16_t* u, uint16_t* h, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        h[i] = (uint16_t)(swiglu2((uint32_t)g[i], (uint32_t)u[i]) & 0xFFFF);
+        h[i] = (uint16_t)(swiglu2_lut(g_silu_lut, (uint32_t)g[i], (uint32_t)u[i]) & 0xFFFF);
 }
 
 __global__ void step_block_scale_kernel(const uint16_t* a16, const float* sgp, uint8_t* sf, int64_t n) {
@@ -379,8 +420,13 @@ hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegPar
     return hipGetLastError();
 }
 
+static void launch_silu_fill(hipStream_t s) {
+    hipLaunchKernelGGL(silu_lut_fill_kernel, dim3(256), dim3(256), 0, s);
+}
+
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, hipStream_t s) {
+    launch_silu_fill(s);
     hipLaunchKernelGGL(swiglu_absmax_kernel, dim3(g.grid), dim3(g.block), 0, s, gate, up, g, ws, tensor_scale,
                        amax_out);
     return hipGetLastError();
@@ -388,6 +434,7 @@ hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const 
 
 hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,
                               uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
+    launch_silu_fill(s);
     hipLaunchKernelGGL(swiglu_pack_kernel, dim3(g.grid), dim3(g.block), 0, s, gate, up, g, tensor_scale, qdata, sfa,
                        g.reverse);
     return hipGetLastError();
@@ -401,6 +448,7 @@ hipError_t launch_step(int which, const void* a, const void* b, const void* c, v
                            (const uint16_t*)c, (uint16_t*)out, n);
         break;
     case STEP_SWIGLU:
+        launch_silu_fill(s);
         hipLaunchKernelGGL(step_swiglu_kernel, grid, block, 0, s, (const uint16_t*)a, (const uint16_t*)b,
                            (uint16_t*)out, n);
         break;

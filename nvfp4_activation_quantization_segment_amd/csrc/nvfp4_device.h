@@ -216,6 +216,31 @@ __device__ __forceinline__ BlockQ block_setup(uint32_t amax_bits16, float s_g, f
     return b;
 }
 
+// d = RN(e4m3(c) * s_g) and r = RN(1/d) for all 128 codes c, the values
+// block_setup computes per block; built once per workgroup so that a block's
+// divisor and reciprocal become one LDS read.
+__device__ __forceinline__ void build_dr_table(float2* dr, float s_g) {
+    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+        const float d = e4m3_value((uint32_t)c) * s_g;
+        dr[c] = make_float2(d, 1.0f / d);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ BlockQ block_setup_tab(uint32_t amax_bits16, float s_g, float rg, bool sg_fast,
+                                                  const float2* dr) {
+    BlockQ b;
+    float a16 = __uint_as_float(amax_bits16 << 16);
+    bool finite = amax_bits16 < 0x7F80u;
+    b.fast = sg_fast && finite;
+    b.sf = b.fast ? block_scale_fast(a16, s_g, rg) : block_scale_slow(a16, s_g);
+    const float2 t = dr[b.sf];
+    b.d = t.x;
+    b.r = t.y;
+    b.keep = (b.sf == 0u || b.sf == 0x7Fu) ? 0u : 0xFFFFFFFFu;
+    return b;
+}
+
 // Packed per-half maximum of two words of two uint16 each (v_pk_max_u16).
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {

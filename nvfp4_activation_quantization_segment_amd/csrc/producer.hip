@@ -82,12 +82,12 @@ __device__ void reduce_and_finish(uint32_t m16, uint32_t* ws, float* tensor_scal
 // One thread, one whole 16-value block: maximum, scale, codes, and the 8
 // QDATA bytes plus the scale byte stored for block b of a row.
 __device__ __forceinline__ void pack_block16_store(const uint32_t y[8], float s_g, float rg, bool sg_fast,
-                                                   uint8_t* __restrict__ qrow, uint8_t* __restrict__ srow,
-                                                   int b) {
+                                                   const float2* dr, uint8_t* __restrict__ qrow,
+                                                   uint8_t* __restrict__ srow, int b) {
     uint32_t m2 = mag2(y[0]);
 #pragma unroll
     for (int k = 1; k < 8; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
-    const BlockQ bq = block_setup(fold_max(m2), s_g, rg, sg_fast);
+    const BlockQ bq = block_setup_tab(fold_max(m2), s_g, rg, sg_fast, dr);
     uint2 w;
     w.x = quantize8(y, bq.d, bq.r, bq.fast) & bq.keep;
     w.y = quantize8(y + 4, bq.d, bq.r, bq.fast) & bq.keep;
@@ -186,7 +186,9 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
                                                              SegParams seg, const float* tensor_scale,
                                                              uint8_t* __restrict__ qdata,
                                                              uint8_t* __restrict__ sfa, int reverse) {
+    __shared__ float2 dr[128];
     const float s_g = tensor_scale[0];
+    build_dr_table(dr, s_g);
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
     const int64_t G = gridDim.x;
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
             uint32_t y[8];
             modulate8(v0, cp0, y);
             modulate8(v1, cp1, y + 4);
-            pack_block16_store(y, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, b);
+            pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
         }
     }
 }
@@ -310,8 +312,10 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ qdata,
                                                            uint8_t* __restrict__ sfa, int reverse) {
     __shared__ __attribute__((aligned(16))) uint16_t slut[65536];
+    __shared__ float2 dr[128];
     lut_to_lds(slut);
     const float s_g = tensor_scale[0];
+    build_dr_table(dr, s_g);
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
     const int64_t G = gridDim.x;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
             uint32_t h[8];
             swiglu8(slut, ld16(gp), ld16(upp), h);
             swiglu8(slut, ld16(gp + 8), ld16(upp + 8), h + 4);
-            pack_block16_store(h, s_g, rg, sg_fast, qdata + r * qld, sfa + r * sld, b);
+            pack_block16_store(h, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
         }
     }
 }

@@ -10,6 +10,13 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts;
 weights are prepacked to NVFP4 (untimed).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Profile summaries (no GPU needed): ``--summarize-trace DIR`` prints the
+kernel table of a ``rocprofv3 --kernel-trace --stats --output-format csv`` run
+of this script; ``--summarize-traffic FETCH_DIR WRITE_DIR`` reads two
+``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs made with
+``--copy-calibration``, prints the per-dispatch table and writes
+``profiles/traffic.json`` for the current GEMM source.
 """
 from __future__ import annotations
 
@@ -38,6 +45,12 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="before timing, copy 1 GiB once (a plain copy kernel of known size, for scaling "
                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
+    p.add_argument("--summarize-trace", metavar="DIR", help="print the kernel table of a rocprofv3 trace run")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarize FETCH_SIZE/WRITE_SIZE runs and write profiles/traffic.json")
+    p.add_argument("--summarize-mfma", metavar="DIR",
+                   help="MFMA busy and clock per GEMM launch from a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                        "SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE run")
     return p.parse_args()
 
 
@@ -68,9 +81,18 @@ def traffic_entry(kernel: str, source_hash: str):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the producer shards by rows with one 4-byte max all-reduce, which this build does not run)",
+              "(a multi-GPU step would shard rows and all-reduce one 4-byte maximum; it is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -335,6 +357,188 @@ def cpu_baseline(args, x_h, segs, gu_h, works):
         "gemm_TFLOPs": round(t_flop / t_gemm / 1e12, 6),
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+PROJ = ("qkv", "fc1", "fc2")  # GEMM launch order within a step
+SHAPES = {"qkv": (37810, 21504, 5376), "fc1": (37810, 14336, 5376), "fc2": (37810, 5376, 14336)}
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_trace(d):
+    import numpy as np
+
+    stats = _csv_rows(d, "kernel_stats.csv")
+    trace = _csv_rows(d, "kernel_trace.csv")
+    out = ["| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "nvfp4::" not in r["Name"]:
+            continue
+        out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    gem = sorted((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                 for r in trace if "gemm_kernel" in r["Kernel_Name"])
+    per = {p: [] for p in PROJ}
+    for i, (_, us) in enumerate(gem):
+        per[PROJ[i % 3]].append(us)
+    out += ["", "| GEMM launch | M, N, K | dispatches | mean us | TFLOP/s | % of 2516.6 |", "|---|---|---|---|---|---|"]
+    tot_f = tot_us = 0.0
+    for p in PROJ:
+        if not per[p]:
+            continue
+        M, N, K = SHAPES[p]
+        us = float(np.mean(per[p]))
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        tot_f += 2.0 * M * N * K * len(per[p])
+        tot_us += sum(per[p])
+        out.append(f"| {p} | {M}, {N}, {K} | {len(per[p])} | {us:.1f} | {tf:.1f} | {100 * tf / MFMA_F16_PEAK_TFLOPS:.1f} |")
+    if tot_us:
+        tf = tot_f / (tot_us * 1e-6) / 1e12
+        out.append(f"| all | | {len(gem)} | {tot_us / len(gem):.1f} | {tf:.1f} | {100 * tf / MFMA_F16_PEAK_TFLOPS:.1f} |")
+    return "\n".join(out)
+
+
+def _counter_by_dispatch(d):
+    rows = _csv_rows(d, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        k = int(r["Dispatch_Id"])
+        e = by.setdefault(k, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "v": 0.0})
+        e["v"] += float(r["Counter_Value"])
+    return by
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM launches, each
+    scaled by what the same counter reads for the 1 GiB calibration copy."""
+    import numpy as np
+
+    f = _counter_by_dispatch(fetch_dir)
+    w = _counter_by_dispatch(write_dir)
+    gib_kib = float(1 << 20)
+
+    def calib(by):
+        """Scale factor and dispatch id of the 1 GiB calibration copy, which
+        runs after the untimed weight prepacks and before the first step."""
+        cps = [(e["v"], k) for k, e in by.items() if "copy" in e["name"].lower() and e["v"] > gib_kib / 4]
+        if not cps:
+            raise SystemExit("no 1 GiB calibration copy found (run bench.py with --copy-calibration)")
+        v, k = max(cps)
+        return gib_kib / v, k
+
+    (fs, f0), (ws, w0) = calib(f), calib(w)
+    f = {k: e for k, e in f.items() if k > f0}
+    w = {k: e for k, e in w.items() if k > w0}
+
+    def gemm_seq(by):
+        return [by[k]["v"] for k in sorted(by) if "gemm_kernel" in by[k]["name"]]
+
+    gf, gw = gemm_seq(f), gemm_seq(w)
+    per = {p: {"fetch": [], "write": []} for p in PROJ}
+    for i, v in enumerate(gf):
+        per[PROJ[i % 3]]["fetch"].append(v * fs * 1024)
+    for i, v in enumerate(gw):
+        per[PROJ[i % 3]]["write"].append(v * ws * 1024)
+    shapes = {}
+    for p in PROJ:
+        M, N, K = SHAPES[p]
+        Mp = (M + 63) // 64 * 64
+        alg = Mp * (K // 2 + K // 16) + N * (K // 2 + K // 16) + M * N * 2
+        shapes[p] = {"fetch": int(np.mean(per[p]["fetch"])), "write": int(np.mean(per[p]["write"])),
+                     "algorithmic_operand_and_output_bytes": alg}
+    bpl = float(np.mean([shapes[p]["fetch"] + shapes[p]["write"] for p in PROJ]))
+    entry = {
+        "bytes_per_launch": int(bpl),
+        "source_hash": src_hash("gemm.hip", "nvfp4_device.h"),
+        "fetch_scale": round(fs, 4),
+        "write_scale": round(ws, 4),
+        "per_shape_bytes": shapes,
+        "note": "FETCH_SIZE and WRITE_SIZE (KiB/dispatch, rocprofv3 --pmc, one counter per run) scaled by the "
+                "readings of a 1 GiB plain copy in the same run; mean over the QKV, FC1 and FC2 launches",
+    }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data["gemm_kernel"] = entry
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1)
+    out = [f"Calibration: 1 GiB copy -> fetch x{fs:.3f}, write x{ws:.3f}.", "",
+           "| kernel | launch | fetch (scaled, MB) | write (scaled, MB) | algorithmic bytes (MB) |",
+           "|---|---|---|---|---|"]
+    for p in PROJ:
+        e = shapes[p]
+        out.append(f"| gemm_kernel | {p} | {e['fetch'] / 1e6:.1f} | {e['write'] / 1e6:.1f} | "
+                   f"{e['algorithmic_operand_and_output_bytes'] / 1e6:.1f} |")
+    prod = {}
+    for k in sorted(f):
+        e = f[k]
+        n = _short(e["name"])
+        if "nvfp4::" in n and "gemm" not in n:
+            prod.setdefault((n, e["grid"]), {"fetch": [], "write": []})["fetch"].append(e["v"] * fs * 1024)
+    for k in sorted(w):
+        e = w[k]
+        n = _short(e["name"])
+        if (n, e["grid"]) in prod:
+            prod[(n, e["grid"])]["write"].append(e["v"] * ws * 1024)
+    for (n, g), e in prod.items():
+        fm = float(np.mean(e["fetch"])) if e["fetch"] else 0.0
+        wm = float(np.mean(e["write"])) if e["write"] else 0.0
+        out.append(f"| {n.replace('nvfp4::', '')} | grid {g} | {fm / 1e6:.1f} | {wm / 1e6:.1f} | |")
+    out.append("")
+    out.append(f"profiles/traffic.json: gemm_kernel bytes_per_launch {int(bpl)} (source hash {entry['source_hash']})")
+    return "\n".join(out)
+
+
+def summarize_mfma(d):
+    """Per GEMM launch: mean engine clock (GRBM_GUI_ACTIVE summed over the 8
+    XCDs / duration) and MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES summed over the
+    1024 SIMDs / 1024 / active cycles).  A v_mfma_f32_32x32x16_f16 keeps a
+    SIMD's matrix core busy 32 cycles, so busy x clock x 1024 SIMDs x 1024
+    flop/cycle is the MFMA rate the counters imply."""
+    import numpy as np
+
+    rows = _csv_rows(d, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        if "gemm_kernel" not in r["Kernel_Name"]:
+            continue
+        e = by.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = {p: [] for p in PROJ}
+    for i, k in enumerate(sorted(by)):
+        per[PROJ[i % 3]].append(by[k])
+    out = ["| GEMM launch | dispatches | mean us (profiled) | clock GHz | MFMA busy | implied TFLOP/s | measured TFLOP/s |",
+           "|---|---|---|---|---|---|---|"]
+    for p in PROJ:
+        if not per[p]:
+            continue
+        M, N, K = SHAPES[p]
+        us = float(np.mean([e["us"] for e in per[p]]))
+        act = float(np.mean([e["GRBM_GUI_ACTIVE"] / 8 for e in per[p]]))
+        busy = float(np.mean([e["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (e["GRBM_GUI_ACTIVE"] / 8) for e in per[p]]))
+        clk = act / (us * 1e3)
+        implied = busy * clk * 1e9 * 1024 * 1024 / 1e12
+        meas = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out.append(f"| {p} | {len(per[p])} | {us:.1f} | {clk:.3f} | {busy:.3f} | {implied:.1f} | {meas:.1f} |")
+    return "\n".join(out)
 
 
 if __name__ == "__main__":

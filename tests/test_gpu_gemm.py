@@ -177,3 +177,35 @@ def test_canonical_projection_sampled_rows(m, name):
     got = out_f64(out[torch.from_numpy(rows).to(dev)])
     worst = check(ref, got, name)
     print(f"{name}: worst err/bound {worst:.3g}", flush=True)
+
+
+def test_scale_rows_misaligned_take_the_word_path(m):
+    """K % 256 == 0 lets the kernel fetch scales 16 bytes per row per 4 K
+    steps, but only when both scale arrays are 16-byte aligned; scale arrays
+    that are only 4-byte aligned take the 4-byte path.  Both give the same
+    bits (the accumulation order does not depend on how scales are loaded)."""
+    dev = device()
+    rng = np.random.default_rng(11)
+    M, N, K = 200, 272, 512
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+
+    def offset_copy(arr, off):
+        buf = torch.zeros(arr.size + 64, dtype=torch.uint8, device=dev)
+        view = buf[off:off + arr.size].view(arr.shape)
+        view.copy_(torch.from_numpy(np.ascontiguousarray(arr)))
+        assert view.data_ptr() % 16 == off % 16
+        return view
+
+    outs = []
+    for off in (0, 4):
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+        m.nvfp4_gemm(to_dev(qa), offset_copy(sfa, off), to_dev(np.array([sa], np.float32)), M, qa.shape[0],
+                     to_dev(qw), offset_copy(sfw, off), to_dev(np.array([sw], np.float32)), N, K, out, N)
+        torch.cuda.synchronize()
+        outs.append(host_u16(out))
+    ref = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    for o in outs:
+        check(ref, (o.astype(np.uint32) << 16).view(np.float32).astype(np.float64), "alignment")
+    assert np.array_equal(outs[0], outs[1])

@@ -251,7 +251,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 e2m1/e4m3 operands, f16 MFMA, fp32 accumulate, bf16 out",
+        "dtype": "f16",
+        "dtype_detail": "NVFP4 (e2m1 values, e4m3 block scales) operands decoded exactly to f16 for the MFMA, "
+                        "fp32 accumulation, bf16 output; producers in binary32 with bf16 roundings",
         "data": "synthetic (seeded; shapes of the H3 block at 37,810 tokens)",
         "config": {
             "workload": "H3 block NVFP4 projections QKV+FC1+FC2, M=37810 (padded 37824): modulation producer "

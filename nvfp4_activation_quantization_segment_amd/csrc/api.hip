@@ -36,7 +36,6 @@ RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int tar
     // rows are visited grid-stride; the grid never exceeds the row count
     const int64_t grid = rows_total < target_wgs ? rows_total : target_wgs;
     g.grid = (int32_t)(grid > 0 ? grid : 1);
-    g.rows_per_wg = (int32_t)((rows_total + g.grid - 1) / g.grid);
     g.reverse = reverse;
     return g;
 }

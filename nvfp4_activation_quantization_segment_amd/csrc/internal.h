@@ -17,18 +17,18 @@ struct SegParams {
     int64_t ld;
 };
 
-// Row-pass geometry: each thread owns 8-column chunks c = threadIdx.x + j*block
-// (j < J); workgroup b visits rows b, b+grid, b+2*grid, ... (grid-stride).
+// Row-pass geometry: each thread owns column chunks c = threadIdx.x + j*block
+// (j < J) of 8 columns in the absmax passes and 16 (one block) in the pack
+// passes; workgroup b visits rows b, b+grid, b+2*grid, ... (grid-stride).
 struct RowGeo {
     int64_t M;            // logical rows
     int64_t rows_total;   // rows the grid covers (M, or M_pad when padding is written)
     int64_t ldx;          // input row stride (elements)
     int32_t C8;           // 8-column chunks per row
-    int32_t J;            // chunks per thread
-    int32_t rows_per_wg;  // ceil(rows_total / grid), informational
+    int32_t J;            // chunks per thread (of the pass's chunk width)
     int32_t grid;
     int32_t block;
-    int32_t reverse;      // pack pass walks row tiles last-to-first
+    int32_t reverse;      // the pass visits rows last-to-first
 };
 
 enum StepKind { STEP_MODULATE, STEP_SWIGLU, STEP_BLOCK_SCALE, STEP_ELEMENT_CODE, STEP_E2M1, STEP_E4M3 };

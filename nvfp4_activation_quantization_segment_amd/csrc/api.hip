@@ -32,9 +32,12 @@ RowGeo row_geo(int64_t M, int64_t rows_total, int64_t width, int64_t ld, int tar
     const int chunks = (int)(width / cols_per_thread);
     g.J = (chunks + 1023) / 1024;
     const int per = (chunks + g.J - 1) / g.J;
-    g.block = (per + 63) / 64 * 64;
-    // rows are visited grid-stride; the grid never exceeds the row count
-    const int64_t grid = rows_total < target_wgs ? rows_total : target_wgs;
+    // pack passes put several short rows in one workgroup so that few lanes idle
+    g.R = (cols_per_thread == 16 && chunks <= 512) ? 1024 / chunks : 1;
+    g.block = (per * g.R + 63) / 64 * 64;
+    // rows are visited grid-stride; the grid never exceeds the row-group count
+    const int64_t groups = (rows_total + g.R - 1) / g.R;
+    const int64_t grid = groups < target_wgs ? groups : target_wgs;
     g.grid = (int32_t)(grid > 0 ? grid : 1);
     g.reverse = reverse;
     return g;

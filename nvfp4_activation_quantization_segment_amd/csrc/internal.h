@@ -19,7 +19,8 @@ struct SegParams {
 
 // Row-pass geometry: each thread owns column chunks c = threadIdx.x + j*block
 // (j < J) of 8 columns in the absmax passes and 16 (one block) in the pack
-// passes; workgroup b visits rows b, b+grid, b+2*grid, ... (grid-stride).
+// passes; workgroup b visits rows b, b+grid, b+2*grid, ... (grid-stride), or
+// in the pack passes R rows per iteration when a row is short.
 struct RowGeo {
     int64_t M;            // logical rows
     int64_t rows_total;   // rows the grid covers (M, or M_pad when padding is written)
@@ -29,6 +30,7 @@ struct RowGeo {
     int32_t grid;
     int32_t block;
     int32_t reverse;      // the pass visits rows last-to-first
+    int32_t R;            // rows per workgroup iteration (pack passes; 1 for absmax)
 };
 
 enum StepKind { STEP_MODULATE, STEP_SWIGLU, STEP_BLOCK_SCALE, STEP_ELEMENT_CODE, STEP_E2M1, STEP_E4M3 };

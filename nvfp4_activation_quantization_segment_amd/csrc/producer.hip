@@ -144,6 +144,7 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
         if (c >= g.C8) break;
         int64_t r = blockIdx.x;
         int s = seg_advance(seg, r < g.M ? r : 0, 0);
+        int64_t seg_end = seg.row_start[s + 1];  // rows only increase: one compare per row
         ColParams cp;
         load_cols(seg, s, c, cp);
         for (; r + 3 * G < g.M; r += 4 * G) {
@@ -152,9 +153,9 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
             for (int u = 0; u < 4; ++u) v[u] = ld16(x + (r + u * G) * g.ldx + 8 * c);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int su = seg_advance(seg, r + u * G, s);
-                if (su != s) {
-                    s = su;
+                if (r + u * G >= seg_end) {
+                    s = seg_advance(seg, r + u * G, s);
+                    seg_end = seg.row_start[s + 1];
                     load_cols(seg, s, c, cp);
                 }
                 uint32_t y[4];
@@ -164,9 +165,9 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
             }
         }
         for (; r < g.M; r += G) {
-            const int su = seg_advance(seg, r, s);
-            if (su != s) {
-                s = su;
+            if (r >= seg_end) {
+                s = seg_advance(seg, r, s);
+                seg_end = seg.row_start[s + 1];
                 load_cols(seg, s, c, cp);
             }
             uint32_t y[4];
@@ -194,29 +195,37 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
     const int64_t G = gridDim.x;
     const int C16 = g.C8 >> 1;
     const int64_t qld = 8 * (int64_t)C16, sld = C16;
+    // a workgroup iteration covers R rows: thread idx takes block idx % C16 of
+    // row offset idx / C16 (R > 1 only when a row has at most 512 blocks)
+    const int64_t GR = G * g.R;
     for (int j = 0; j < g.J; ++j) {
-        const int b = threadIdx.x + j * blockDim.x;
-        if (b >= C16) break;
+        const int idx = threadIdx.x + j * blockDim.x;
+        const int rho = idx / C16;
+        const int b = idx - rho * C16;
+        if (rho >= g.R) break;
         // padding rows M .. rows_total-1 are zero
-        for (int64_t r = g.M + blockIdx.x; r < g.rows_total; r += G) {
+        for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
             *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
             sfa[r * sld + b] = 0;
         }
-        int64_t i = blockIdx.x;
+        int64_t i = (int64_t)blockIdx.x * g.R + rho;
         if (i >= g.M) continue;
         int64_t r = reverse ? g.M - 1 - i : i;
         int s = 0;
         while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
+        int64_t seg_lo = seg.row_start[s], seg_hi = seg.row_start[s + 1];
         ColParams cp0, cp1;
         load_cols(seg, s, 2 * b, cp0);
         load_cols(seg, s, 2 * b + 1, cp1);
-        for (; i < g.M; i += G) {
+        for (; i < g.M; i += GR) {
             r = reverse ? g.M - 1 - i : i;
             const uint16_t* xp = x + r * g.ldx + 16 * b;
             const uint4 v0 = ld16(xp), v1 = ld16(xp + 8);
-            if (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) {
+            if (r < seg_lo || r >= seg_hi) {
                 s = 0;
                 while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
+                seg_lo = seg.row_start[s];
+                seg_hi = seg.row_start[s + 1];
                 load_cols(seg, s, 2 * b, cp0);
                 load_cols(seg, s, 2 * b + 1, cp1);
             }
@@ -321,14 +330,17 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
     const int64_t G = gridDim.x;
     const int C16 = g.C8 >> 1;
     const int64_t qld = 8 * (int64_t)C16, sld = C16;
+    const int64_t GR = G * g.R;
     for (int j = 0; j < g.J; ++j) {
-        const int b = threadIdx.x + j * blockDim.x;
-        if (b >= C16) break;
-        for (int64_t r = g.M + blockIdx.x; r < g.rows_total; r += G) {
+        const int idx = threadIdx.x + j * blockDim.x;
+        const int rho = idx / C16;
+        const int b = idx - rho * C16;
+        if (rho >= g.R) break;
+        for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
             *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
             sfa[r * sld + b] = 0;
         }
-        for (int64_t i = blockIdx.x; i < g.M; i += G) {
+        for (int64_t i = (int64_t)blockIdx.x * g.R + rho; i < g.M; i += GR) {
             const int64_t r = reverse ? g.M - 1 - i : i;
             const uint16_t* gp = gate + r * g.ldx + 16 * b;
             const uint16_t* upp = up + r * g.ldx + 16 * b;

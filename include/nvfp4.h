@@ -48,6 +48,10 @@
  *    non-finite tensor scale, which the caller can test.
  *  - Calls that share a workspace or outputs must not overlap in time (for
  *    example on two streams without ordering between them).
+ *  - The SwiGLU entry points first enqueue a small kernel that fills a
+ *    65,536-entry bf16 silu table held in the library's own module-scope
+ *    device memory (128 KB per device, part of the code object, not an
+ *    allocation); calls overlapping on other streams write identical values.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

@@ -139,7 +139,10 @@ def main():
             amax=torch.empty(1, dtype=torch.float32, device=dev),
             out=torch.empty((M, w.N), dtype=torch.bfloat16, device=dev),
             ws=torch.zeros(int(nv.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev),
+            gws_bytes=nv.nvfp4_gemm_workspace_bytes(M, w.N, K),
         )
+        b = bufs[w.name]
+        b["gws"] = torch.empty(max(b["gws_bytes"], 16), dtype=torch.uint8, device=dev)
     seg_structs = {n: nv.make_segments(*segs[n]) for n in segs}
     F = wf2.K
     gate_ptr, up_ptr = gu.data_ptr(), gu.data_ptr() + 2 * F
@@ -160,8 +163,9 @@ def main():
                         lambda b=b, seg=seg, w=w: nv.nvfp4_modulate_pack(x, M, w.K, w.K, seg, b["ts"], b["q"],
                                                                          b["s"], M_pad, stream)))
             seq.append((f"{w.name}.gemm", "gemm",
-                        lambda b=b, w=w, qw=qw, sfw=sfw, tw=tw: nv.nvfp4_gemm(
-                            b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, w.N, w.K, b["out"], w.N, stream)))
+                        lambda b=b, w=w, qw=qw, sfw=sfw, tw=tw: nv.nvfp4_gemm_ws(
+                            b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, w.N, w.K, b["out"], w.N, b["gws"],
+                            b["gws_bytes"], stream)))
         b = bufs["fc2"]
         qw, sfw, tw = weights["fc2"]
         seq.append(("fc2.absmax", "swiglu_absmax",
@@ -171,8 +175,8 @@ def main():
                     lambda: nv.nvfp4_swiglu_pack(gate_ptr, up_ptr, M, F, 2 * F, b["ts"], b["q"], b["s"], M_pad,
                                                  stream)))
         seq.append(("fc2.gemm", "gemm",
-                    lambda: nv.nvfp4_gemm(b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, wf2.N, wf2.K, b["out"],
-                                          wf2.N, stream)))
+                    lambda: nv.nvfp4_gemm_ws(b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, wf2.N, wf2.K, b["out"],
+                                             wf2.N, b["gws"], b["gws_bytes"], stream)))
         return seq
 
     seq = launches()
@@ -263,7 +267,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_kernel (3 launches per step: QKV, FC1, FC2)",
+            "kernel": "nvfp4_gemm_ws: gemm_kernel per projection (QKV, FC1, FC2; FC2 adds a K-split launch for its "
+                      "last partial wave and a finalize launch); achieved = per-projection call time",
             "achieved": round(gemm_achieved, 1),
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -368,6 +373,31 @@ PROJ = ("qkv", "fc1", "fc2")  # GEMM launch order within a step
 SHAPES = {"qkv": (37810, 21504, 5376), "fc1": (37810, 14336, 5376), "fc2": (37810, 5376, 14336)}
 
 
+def _gemm_role(name):
+    """'main', 'split' or 'finalize' for the GEMM kernels, else None."""
+    if "gemm_finalize_kernel" in name:
+        return "finalize"
+    if "gemm_kernel" not in name:
+        return None
+    args = name.split("gemm_kernel<", 1)[1].split(">", 1)[0].split(",") if "gemm_kernel<" in name else []
+    return "split" if len(args) > 1 and args[1].strip() == "true" else "main"
+
+
+def _gemm_calls(items):
+    """Group GEMM dispatches (in dispatch order) into calls: a main launch
+    starts a call, split and finalize launches belong to the call before them.
+    items: (dispatch_id, kernel_name, payload).  Returns [(projection, [payloads])]."""
+    calls = []
+    for _, name, payload in sorted(items, key=lambda t: t[0]):
+        role = _gemm_role(name)
+        if role is None:
+            continue
+        if role == "main" or not calls:
+            calls.append([])
+        calls[-1].append(payload)
+    return [(PROJ[i % 3], c) for i, c in enumerate(calls)]
+
+
 def _csv_rows(d, suffix):
     import csv
     import glob
@@ -397,12 +427,14 @@ def summarize_trace(d):
             continue
         out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-    gem = sorted((int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-                 for r in trace if "gemm_kernel" in r["Kernel_Name"])
+    calls = _gemm_calls([(int(r["Dispatch_Id"]), r["Kernel_Name"],
+                          (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace])
     per = {p: [] for p in PROJ}
-    for i, (_, us) in enumerate(gem):
-        per[PROJ[i % 3]].append(us)
-    out += ["", "| GEMM launch | M, N, K | dispatches | mean us | TFLOP/s | % of 2516.6 |", "|---|---|---|---|---|---|"]
+    for p, c in calls:
+        per[p].append(sum(c))
+    gem = [u for p in PROJ for u in per[p]]
+    out += ["", "GEMM calls (main launch plus, for FC2, the K-split launch and the finalize launch):", "",
+            "| GEMM call | M, N, K | calls | mean us | TFLOP/s | % of 2516.6 |", "|---|---|---|---|---|---|"]
     tot_f = tot_us = 0.0
     for p in PROJ:
         if not per[p]:
@@ -451,15 +483,11 @@ def summarize_traffic(fetch_dir, write_dir):
     f = {k: e for k, e in f.items() if k > f0}
     w = {k: e for k, e in w.items() if k > w0}
 
-    def gemm_seq(by):
-        return [by[k]["v"] for k in sorted(by) if "gemm_kernel" in by[k]["name"]]
-
-    gf, gw = gemm_seq(f), gemm_seq(w)
     per = {p: {"fetch": [], "write": []} for p in PROJ}
-    for i, v in enumerate(gf):
-        per[PROJ[i % 3]]["fetch"].append(v * fs * 1024)
-    for i, v in enumerate(gw):
-        per[PROJ[i % 3]]["write"].append(v * ws * 1024)
+    for p, c in _gemm_calls([(k, e["name"], e["v"]) for k, e in f.items()]):
+        per[p]["fetch"].append(sum(c) * fs * 1024)
+    for p, c in _gemm_calls([(k, e["name"], e["v"]) for k, e in w.items()]):
+        per[p]["write"].append(sum(c) * ws * 1024)
     shapes = {}
     for p in PROJ:
         M, N, K = SHAPES[p]
@@ -520,14 +548,18 @@ def summarize_mfma(d):
     rows = _csv_rows(d, "counter_collection.csv")
     by = {}
     for r in rows:
-        if "gemm_kernel" not in r["Kernel_Name"]:
+        if _gemm_role(r["Kernel_Name"]) is None:
             continue
-        e = by.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                 "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     per = {p: [] for p in PROJ}
-    for i, k in enumerate(sorted(by)):
-        per[PROJ[i % 3]].append(by[k])
-    out = ["| GEMM launch | dispatches | mean us (profiled) | clock GHz | MFMA busy | implied TFLOP/s | measured TFLOP/s |",
+    for p, c in _gemm_calls([(k, e["name"], e) for k, e in by.items()]):
+        tot = {"us": sum(x["us"] for x in c)}
+        for key in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES"):
+            tot[key] = sum(x.get(key, 0.0) for x in c)
+        per[p].append(tot)
+    out = ["| GEMM call | calls | mean us (profiled) | clock GHz | MFMA busy | implied TFLOP/s | measured TFLOP/s |",
            "|---|---|---|---|---|---|---|"]
     for p in PROJ:
         if not per[p]:

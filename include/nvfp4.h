@@ -153,6 +153,26 @@ nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_sc
                         int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
                         int64_t N, int64_t K, uint16_t* out, int64_t ldo, void* stream);
 
+/* Bytes of device workspace nvfp4_gemm_ws uses for an [M,K] x [N,K] product
+ * (0 when it has nothing to split).  Depends on the shape only. */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* nvfp4_gemm with a caller-owned workspace of at least
+ * nvfp4_gemm_workspace_bytes(M, N, K) bytes (16-byte aligned; may be NULL when
+ * that is 0).  The output tiles are computed in waves of 256 workgroups; when
+ * the last wave would fill at most a third of the chip, its tiles are each
+ * computed as several K ranges by separate workgroups whose binary32 partial
+ * sums land in the workspace, then added in K order and scaled by alpha.  The
+ * result satisfies the same contract as nvfp4_gemm (only the binary32
+ * summation order differs).  The workspace holds no state between calls;
+ * calls sharing it must not overlap.  Same requirements and errors as
+ * nvfp4_gemm, plus NVFP4_ERR_INVALID_ARGUMENT for a missing or short
+ * workspace. */
+nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
+                           int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
+                           int64_t N, int64_t K, uint16_t* out, int64_t ldo, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ---- Single-step entry points ------------------------------------------
  * Elementwise versions of single producer steps, running the very device
  * functions the producer kernels use, so that each step can be checked over

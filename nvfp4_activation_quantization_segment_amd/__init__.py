@@ -54,6 +54,8 @@ def _load():
         "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
         "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
         "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
+        "nvfp4_gemm_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64]),
+        "nvfp4_gemm_ws": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, P, ctypes.c_size_t, V]),
         "nvfp4_step_modulate": (I32, [P, P, P, P, I64, V]),
         "nvfp4_step_swiglu": (I32, [P, P, P, I64, V]),
         "nvfp4_step_block_scale": (I32, [P, P, P, I64, V]),
@@ -166,6 +168,17 @@ def nvfp4_gemm(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, str
                           _ptr(out), ldo, _stream(stream)))
 
 
+def nvfp4_gemm_workspace_bytes(M, N, K):
+    return int(lib.nvfp4_gemm_workspace_bytes(M, N, K))
+
+
+def nvfp4_gemm_ws(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, workspace, workspace_bytes,
+                  stream=None):
+    _check("nvfp4_gemm_ws",
+           lib.nvfp4_gemm_ws(_ptr(qa), _ptr(sfa), _ptr(a_scale), M, M_pad, _ptr(qw), _ptr(sfw), _ptr(w_scale), N, K,
+                             _ptr(out), ldo, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def nvfp4_step_modulate(x, scale, shift, y, n, stream=None):
     _check("nvfp4_step_modulate",
            lib.nvfp4_step_modulate(_ptr(x), _ptr(scale), _ptr(shift), _ptr(y), n, _stream(stream)))
@@ -244,12 +257,20 @@ def quantize_weight(w: torch.Tensor, stream=None):
     return q[:N], s[:N], ts
 
 
-def gemm(qa, sfa, a_scale, M: int, qw, sfw, w_scale, out: torch.Tensor | None = None, stream=None):
-    """out [M, N] bf16 = bf16(a_scale * w_scale * dequant(qa) dequant(qw)^T)."""
+def gemm(qa, sfa, a_scale, M: int, qw, sfw, w_scale, out: torch.Tensor | None = None, stream=None,
+         workspace: torch.Tensor | None = None):
+    """out [M, N] bf16 = bf16(a_scale * w_scale * dequant(qa) dequant(qw)^T).
+
+    Runs nvfp4_gemm_ws; a workspace of nvfp4_gemm_workspace_bytes(M, N, K)
+    bytes is allocated with torch when none is given."""
     M_pad, Kh = qa.shape
     N = qw.shape[0]
     K = 2 * Kh
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
-    nvfp4_gemm(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, out.stride(0), stream)
+    need = nvfp4_gemm_workspace_bytes(M, N, K)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
+    nvfp4_gemm_ws(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, out.stride(0), workspace,
+                  need, stream)
     return out

@@ -159,9 +159,9 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
     return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
 }
 
-nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
-                        const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N, int64_t K,
-                        uint16_t* out, int64_t ldo, void* stream) {
+static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
+                              int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N,
+                              int64_t K, uint16_t* out, int64_t ldo, GemmArgs* a) {
     if (!qa || !sfa || !a_scale || !qw || !sfw || !w_scale || !out) return NVFP4_ERR_INVALID_ARGUMENT;
     if (M <= 0 || N <= 0 || K <= 0 || ldo < N || M_pad < M) return NVFP4_ERR_INVALID_ARGUMENT;
     if (K % 64 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
@@ -171,20 +171,49 @@ nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_sc
     if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sfa, 4) || !aligned(sfw, 4) || !aligned(out, 8) ||
         ldo % 4 != 0 || !aligned(a_scale, 4) || !aligned(w_scale, 4))
         return NVFP4_ERR_ALIGNMENT;
+    a->qa = qa;
+    a->sfa = sfa;
+    a->a_scale = a_scale;
+    a->qw = qw;
+    a->sfw = sfw;
+    a->w_scale = w_scale;
+    a->out = out;
+    a->ldo = ldo;
+    a->M = (int32_t)M;
+    a->M_pad = (int32_t)M_pad;
+    a->N = (int32_t)N;
+    a->K = (int32_t)K;
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
+                        const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N, int64_t K,
+                        uint16_t* out, int64_t ldo, void* stream) {
     GemmArgs a;
-    a.qa = qa;
-    a.sfa = sfa;
-    a.a_scale = a_scale;
-    a.qw = qw;
-    a.sfw = sfw;
-    a.w_scale = w_scale;
-    a.out = out;
-    a.ldo = ldo;
-    a.M = (int32_t)M;
-    a.M_pad = (int32_t)M_pad;
-    a.N = (int32_t)N;
-    a.K = (int32_t)K;
-    return hip_status(launch_gemm(a, (hipStream_t)stream));
+    const nvfp4_status st = gemm_args(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, &a);
+    if (st != NVFP4_OK) return st;
+    return hip_status(launch_gemm(a, nullptr, false, (hipStream_t)stream));
+}
+
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) ||
+        K >= ((int64_t)1 << 31))
+        return 0;
+    return gemm_plan(M, N, K).workspace_bytes;
+}
+
+nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
+                           const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N, int64_t K,
+                           uint16_t* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+    GemmArgs a;
+    const nvfp4_status st = gemm_args(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, &a);
+    if (st != NVFP4_OK) return st;
+    const size_t need = gemm_plan(M, N, K).workspace_bytes;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return NVFP4_ERR_INVALID_ARGUMENT;
+        if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGNMENT;
+    }
+    return hip_status(launch_gemm(a, (float*)workspace, need > 0, (hipStream_t)stream));
 }
 
 static nvfp4_status step(int which, const void* a, const void* b, const void* c, void* out, int64_t n,

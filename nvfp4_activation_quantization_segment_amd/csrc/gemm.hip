@@ -41,6 +41,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 128, kWN = 64;
+// Workgroup slots of one wave over the chip (256 CUs, one 512-thread workgroup each).
+constexpr int kWaveSlots = 256;
 
 // Raw E4M3 bits of byte `b` of a scale word, as two fp16 equal to sf * 2^-8.
 __device__ __forceinline__ uint32_t sf_raw2(uint32_t word, int b) {
@@ -185,24 +187,43 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
     __syncthreads();
 }
 
-template <bool SC4>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
-gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
-
-    // Tile order: each XCD (workgroups are dealt round-robin over 8) takes a
-    // contiguous range of tiles, walked in groups of 4 M-tiles so that the
-    // workgroups resident on one XCD share activation and weight rows in L2.
-    const int T = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int per = T / 8;
-    const int logical = (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
+// Output tile of logical tile index `logical`: tiles are walked in groups of
+// 4 M-tiles (all N-tiles of a group before the next group), so that the
+// workgroups resident on one XCD share activation and weight rows in L2.
+__device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
     constexpr int GM = 4;
     const int gsz = GM * tiles_n;
     const int first_m = (logical / gsz) * GM;
     const int gm = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-    const int tm = first_m + (logical % gsz) % gm;
-    const int tn = (logical % gsz) / gm;
+    tm = first_m + (logical % gsz) % gm;
+    tn = (logical % gsz) / gm;
+}
+
+// One launch's share of the output tiles.  The main launch computes tiles
+// [0, tiles) over all of K; a split launch computes `tiles` tail tiles from
+// tile_base on, each as ksplit K ranges of ks steps, and stores fp32 partial
+// sums for gemm_finalize_kernel.
+template <bool SC4, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
+gemm_kernel(GemmArgs a, GemmPart p) {
+    __shared__ __attribute__((aligned(16))) _Float16 lds[kLdsBytes / 2];
+
+    // Tile order: in the main launch each XCD (workgroups are dealt
+    // round-robin over 8) takes a contiguous range of logical tiles.
+    const int bid = blockIdx.x;
+    int logical, k0 = 0, nit = a.K / kBK, split = 0, tail = 0;
+    if (!SPLIT) {
+        const int per = p.tiles / 8;
+        logical = (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
+    } else {
+        tail = bid / p.ksplit;
+        split = bid - tail * p.ksplit;
+        logical = p.tile_base + tail;
+        k0 = split * p.ks;
+        nit = nit - k0 < p.ks ? nit - k0 : p.ks;
+    }
+    int tm, tn;
+    tile_coords(logical, p.tiles_m, p.tiles_n, tm, tn);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -231,8 +252,8 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
                 row = tn * kBN + lr + 32 * i;
                 row = row < a.N ? row : a.N - 1;
             }
-            qo[i] = (uint32_t)row * Kb + 16u * sh;
-            so[i] = (uint32_t)row * Ks;
+            qo[i] = (uint32_t)row * Kb + 16u * sh + 32u * (uint32_t)k0;
+            so[i] = (uint32_t)row * Ks + 4u * (uint32_t)k0;
         }
         st.q0 = qo[0];
         st.q1 = qo[1];
@@ -251,7 +272,6 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
         for (int k = 0; k < 4; ++k) acc[i][k] = (f32x16){0};
     const int wrow0 = wn * kWN + l32;
     const int arow0 = wm * kWM + l32;
-    const int nit = a.K / kBK;
     const int ngrp = (nit + 3) / 4;
     const int lastst = nit - 1;
 
@@ -312,6 +332,24 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
         }
     }
 
+    if (SPLIT) {
+        // fp32 partial sums: slot (tail, split), then wave, accumulator quad
+        // (4 consecutive registers = 4 consecutive n), lane; each float4
+        // store of a wave writes 1 KB contiguously.
+        float4* dst = reinterpret_cast<float4*>(p.partial) +
+                      ((size_t)(tail * p.ksplit + split) * 8 + wave) * (32 * 64) + lane;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& c = acc[i][k];
+                    dst[((i * 4 + k) * 4 + q) * 64] = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+                }
+        return;
+    }
+
     // Epilogue: alpha = RN(s_a * s_w) applied in fp32, then bf16 (nearest-even).
     const float alpha = a.a_scale[0] * a.w_scale[0];
 #pragma unroll
@@ -335,18 +373,123 @@ gemm_kernel(GemmArgs a, int tiles_m, int tiles_n) {
     }
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-    const int tiles_m = (a.M + kBM - 1) / kBM;
-    const int tiles_n = (a.N + kBN - 1) / kBN;
+// Sums the ksplit partials of each tail tile in split order, applies alpha
+// and writes bf16 with the main epilogue's layout.  One 64-thread workgroup
+// per (tail tile, wave, 32-row group k): 8 output quads per lane, the partial
+// loads of a quad issued together.
+constexpr int kMaxSplit = 16;
+__global__ __launch_bounds__(64) void gemm_finalize_kernel(GemmArgs a, GemmPart p) {
+    const int tail = blockIdx.x >> 5;
+    const int wave = (blockIdx.x >> 2) & 7;
+    const int k = blockIdx.x & 3;
+    int tm, tn;
+    tile_coords(p.tile_base + tail, p.tiles_m, p.tiles_n, tm, tn);
+    const int lane = threadIdx.x;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int m = tm * kBM + wm * kWM + k * 32 + l32;
+    if (m >= a.M) return;
+    const float alpha = a.a_scale[0] * a.w_scale[0];
+    const size_t slot = (size_t)8 * 32 * 64;  // float4 per partial tile
+    const float4* src = reinterpret_cast<const float4*>(p.partial) + (size_t)tail * p.ksplit * slot +
+                        (size_t)wave * (32 * 64) + lane;
+    uint16_t* orow = a.out + (int64_t)m * a.ldo;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = tn * kBN + wn * kWN + i * 32 + 8 * q + 4 * h;
+            if (n >= a.N) continue;
+            const float4* pe = src + ((i * 4 + k) * 4 + q) * 64;
+            float4 v[kMaxSplit];
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp)
+                if (sp < p.ksplit) v[sp] = pe[(size_t)sp * slot];
+            float4 acc = v[0];
+#pragma unroll
+            for (int sp = 1; sp < kMaxSplit; ++sp)
+                if (sp < p.ksplit) {
+                    acc.x += v[sp].x;
+                    acc.y += v[sp].y;
+                    acc.z += v[sp].z;
+                    acc.w += v[sp].w;
+                }
+            uint2 w;
+            w.x = pack_bf16x2(acc.x * alpha, acc.y * alpha);
+            w.y = pack_bf16x2(acc.z * alpha, acc.w * alpha);
+            *reinterpret_cast<uint2*>(orow + n) = w;
+        }
+    }
+}
+
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K) {
+    GemmPlan pl;
+    pl.tiles_m = (int)((M + kBM - 1) / kBM);
+    pl.tiles_n = (int)((N + kBN - 1) / kBN);
+    const int T = pl.tiles_m * pl.tiles_n;
+    const int nit = (int)(K / kBK);
+    pl.full = T;
+    pl.tail = 0;
+    pl.ksplit = 1;
+    pl.ks = nit;
+    pl.workspace_bytes = 0;
+    // A last wave of at most a third of the workgroup slots is split along K
+    // into as many pieces as fill the slots, each at least 4 K steps and a
+    // multiple of 4 (whole scale groups).
+    const int R = T % kWaveSlots;
+    if (R == 0 || 3 * R > kWaveSlots) return pl;
+    int S = kWaveSlots / R;
+    if (S > kMaxSplit) S = kMaxSplit;
+    if (S > nit / 4) S = nit / 4;
+    if (S < 2) return pl;
+    int ks = (nit + S - 1) / S;
+    ks = (ks + 3) / 4 * 4;
+    S = (nit + ks - 1) / ks;
+    if (S < 2) return pl;
+    pl.full = T - R;
+    pl.tail = R;
+    pl.ksplit = S;
+    pl.ks = ks;
+    pl.workspace_bytes = (size_t)R * S * 8 * 32 * 64 * sizeof(float4);
+    return pl;
+}
+
+static bool scales_16b(const GemmArgs& a) {
     // 16-byte scale-group loads need every scale row and both base pointers
     // 16-byte aligned, i.e. K/16 a multiple of 16.
-    const bool sc4 = (a.K >> 4) % 16 == 0 &&
-                     ((reinterpret_cast<uintptr_t>(a.sfa) | reinterpret_cast<uintptr_t>(a.sfw)) & 15) == 0;
-    if (sc4)
-        hipLaunchKernelGGL(gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL(gemm_kernel<false>, dim3(tiles_m * tiles_n), dim3(512), 0, s, a, tiles_m, tiles_n);
+    return (a.K >> 4) % 16 == 0 &&
+           ((reinterpret_cast<uintptr_t>(a.sfa) | reinterpret_cast<uintptr_t>(a.sfw)) & 15) == 0;
+}
+
+template <bool SC4>
+static hipError_t launch_all(const GemmArgs& a, const GemmPlan& pl, float* workspace, hipStream_t s) {
+    GemmPart p;
+    p.tiles_m = pl.tiles_m;
+    p.tiles_n = pl.tiles_n;
+    p.tile_base = 0;
+    p.tiles = pl.full;
+    p.ksplit = 1;
+    p.ks = pl.ks;
+    p.partial = workspace;
+    if (pl.full > 0)
+        hipLaunchKernelGGL((gemm_kernel<SC4, false>), dim3(pl.full), dim3(512), 0, s, a, p);
+    if (pl.tail > 0) {
+        p.tile_base = pl.full;
+        p.tiles = pl.tail;
+        p.ksplit = pl.ksplit;
+        hipLaunchKernelGGL((gemm_kernel<SC4, true>), dim3(pl.tail * pl.ksplit), dim3(512), 0, s, a, p);
+        hipLaunchKernelGGL(gemm_finalize_kernel, dim3(pl.tail * 32), dim3(64), 0, s, a, p);
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, float* workspace, bool split, hipStream_t s) {
+    GemmPlan pl = gemm_plan(a.M, a.N, a.K);
+    if (!split || !workspace) {
+        pl.full = pl.tiles_m * pl.tiles_n;
+        pl.tail = 0;
+    }
+    return scales_16b(a) ? launch_all<true>(a, pl, workspace, s) : launch_all<false>(a, pl, workspace, s);
 }
 
 }  // namespace nvfp4

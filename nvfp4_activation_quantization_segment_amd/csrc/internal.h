@@ -56,6 +56,22 @@ struct GemmArgs {
     int64_t ldo;
     int32_t M, M_pad, N, K;
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Tiles of one GEMM launch (see gemm.hip).
+struct GemmPart {
+    int32_t tiles_m, tiles_n;
+    int32_t tile_base;  // first logical tile of a split launch
+    int32_t tiles;      // tiles of the launch (main) or tail tiles (split)
+    int32_t ksplit;     // K pieces per tail tile
+    int32_t ks;         // K steps (of 64) per piece
+    float* partial;     // fp32 partial sums of the tail pieces
+};
+// How a GEMM is cut: `full` tiles over all of K, then `tail` tiles in
+// `ksplit` K pieces of `ks` steps, summed by a finalize kernel.
+struct GemmPlan {
+    int tiles_m, tiles_n, full, tail, ksplit, ks;
+    size_t workspace_bytes;
+};
+GemmPlan gemm_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmArgs& a, float* workspace, bool split, hipStream_t s);
 
 }  // namespace nvfp4

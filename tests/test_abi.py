@@ -70,6 +70,31 @@ def test_gemm_argument_errors(pkg):
     assert g(P, P, P, 10, 64, P, P, P, 64, 64, P, 66, None) == 3       # ldo % 4
 
 
+def test_gemm_workspace_plan(pkg):
+    """The split of the last workgroup wave depends on the shape only: of the
+    projection GEMMs only FC2 (3108 tiles of 256x256 = 12 waves of 256 and 36
+    tiles) splits, its 36 tail tiles into 7 K ranges of 32 steps."""
+    wsb = pkg.lib.nvfp4_gemm_workspace_bytes
+    tile = 8 * 128 * 64 * 4  # fp32 partial sums of one 256x256 tile
+    assert wsb(37810, 21504, 5376) == 0      # 12432 tiles: tail of 144 > 256/3
+    assert wsb(37810, 14336, 5376) == 0      # 8288 tiles: tail of 96 > 256/3
+    assert wsb(37810, 5376, 14336) == 36 * 7 * tile
+    assert wsb(1, 16, 64) == 0               # one K step: nothing to split
+    assert wsb(64, 16, 5376) == 11 * tile    # one tile, 84 steps in 11 ranges of 8
+    assert wsb(10, 16, 48) == 0              # invalid K
+
+
+def test_gemm_ws_argument_errors(pkg):
+    g = pkg.lib.nvfp4_gemm_ws
+    P = FAKE
+    need = pkg.lib.nvfp4_gemm_workspace_bytes(64, 16, 5376)
+    assert need > 0
+    assert g(P, P, P, 64, 64, P, P, P, 16, 5376, P, 16, None, need, None) == 1        # no workspace
+    assert g(P, P, P, 64, 64, P, P, P, 16, 5376, P, 16, P, need - 1, None) == 1       # short workspace
+    assert g(P, P, P, 64, 64, P, P, P, 16, 5376, P, 16, P + 4, need, None) == 3       # workspace alignment
+    assert g(P, P, P, 10, 64, P, P, P, 64, 48, P, 64, P, 1 << 20, None) == 2          # K % 64, as nvfp4_gemm
+
+
 def test_producer_argument_errors(pkg):
     L = pkg.lib
     seg, keep = _seg(pkg, [0, 10])

@@ -209,3 +209,51 @@ def test_scale_rows_misaligned_take_the_word_path(m):
     for o in outs:
         check(ref, (o.astype(np.uint32) << 16).view(np.float32).astype(np.float64), "alignment")
     assert np.array_equal(outs[0], outs[1])
+
+
+def gpu_gemm_ws(m, sa, qa, sfa, sw, qw, sfw, M, workspace_pad=0):
+    dev = device()
+    N = qw.shape[0]
+    K = 2 * qw.shape[1]
+    need = m.nvfp4_gemm_workspace_bytes(M, N, K)
+    ws = torch.full((need + workspace_pad,), 0xFF, dtype=torch.uint8, device=dev) if need else None
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    m.nvfp4_gemm_ws(to_dev(qa), to_dev(sfa), to_dev(np.array([sa], np.float32)), M, qa.shape[0], to_dev(qw),
+                    to_dev(sfw), to_dev(np.array([sw], np.float32)), N, K, out, N, ws, need)
+    torch.cuda.synchronize()
+    return out, need
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 16, 5376), (130, 528, 14336), (257, 1024, 512), (600, 4096, 1024), (300, 272, 128), (1, 16, 64),
+])
+def test_split_tail_small_shapes(m, M, N, K):
+    """nvfp4_gemm_ws on shapes whose single partial wave is split along K
+    (and two that are not split), every output against the FP64 oracle."""
+    rng = np.random.default_rng(3 * M + N + K)
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    out, need = gpu_gemm_ws(m, sa, qa, sfa, sw, qw, sfw, M)
+    print(f"{M}x{N}x{K}: workspace {need} bytes", flush=True)
+    check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), out_f64(out), f"ws {M}x{N}x{K}")
+
+
+def test_split_tail_after_full_waves(m):
+    """272 tiles = one full wave of 256 and 16 tail tiles (the last M-tile row),
+    each split into 4 K ranges.  Tiles of the full wave are bit-identical to
+    nvfp4_gemm; the tail rows match the oracle."""
+    rng = np.random.default_rng(17)
+    M, N, K = 17 * 256, 16 * 256, 1024
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    out_ws, need = gpu_gemm_ws(m, sa, qa, sfa, sw, qw, sfw, M, workspace_pad=4096)
+    assert need == 16 * 4 * 8 * 128 * 64 * 4
+    out_plain = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M)
+    got_ws, got_plain = host_u16(out_ws), host_u16(out_plain)
+    assert np.array_equal(got_ws[:16 * 256], got_plain[:16 * 256])
+    rows = np.concatenate([np.arange(16 * 256, M, 3), np.array([0, 1, 255, 4095])])
+    ref = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, rows)
+    check(ref, (got_ws[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64), "tail rows")
+    check(ref, (got_plain[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64), "plain rows")

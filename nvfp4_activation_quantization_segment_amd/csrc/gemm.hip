@@ -31,6 +31,12 @@
 // Measured on the projection shapes this halves the L1 accesses and L2
 // requests of a one-row-per-lane layout, whose vector memory path was close to
 // saturation; the energy saved shows up as clock under the power limit.
+//
+// Waves of tiles.  Tiles run in waves of one workgroup per CU.  With a
+// workspace, a last wave that would leave most CUs idle is computed instead as
+// several K ranges per tile (gemm_plan); the pieces store fp32 partial sums and
+// gemm_finalize_kernel adds them in K order before the alpha and the bf16
+// rounding.
 #include "internal.h"
 #include "nvfp4_device.h"
 

@@ -235,6 +235,10 @@ gemm_kernel(GemmArgs a, GemmPart p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, l32 = lane & 31;
+    // The two waves of a SIMD (w and w+4) run the same instruction stream;
+    // giving one of them a higher issue priority breaks the tie, so one runs
+    // ahead and the other fills its gaps (measured +2-3% over equal priority).
+    if (wave < 4) __builtin_amdgcn_s_setprio(2);
     const uint32_t Kb = (uint32_t)a.K >> 1, Ks = (uint32_t)a.K >> 4;
 
     // Staging role: lane 2r+sh of wave w holds half sh of rows r and r+32 of

@@ -226,6 +226,7 @@ def gpu_gemm_ws(m, sa, qa, sfa, sw, qw, sfw, M, workspace_pad=0):
 
 @pytest.mark.parametrize("M,N,K", [
     (64, 16, 5376), (130, 528, 14336), (257, 1024, 512), (600, 4096, 1024), (300, 272, 128), (1, 16, 64),
+    (200, 512, 640),  # K/16 = 40: 4-byte scale path inside the K-split pieces (pieces of 8 and 2 steps)
 ])
 def test_split_tail_small_shapes(m, M, N, K):
     """nvfp4_gemm_ws on shapes whose single partial wave is split along K
@@ -257,3 +258,29 @@ def test_split_tail_after_full_waves(m):
     ref = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, rows)
     check(ref, (got_ws[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64), "tail rows")
     check(ref, (got_plain[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64), "plain rows")
+
+
+def test_split_tail_with_4byte_aligned_scales(m):
+    """The K-split pieces with scale arrays that are only 4-byte aligned (the
+    per-step scale path, offset to each piece's first K step)."""
+    dev = device()
+    rng = np.random.default_rng(23)
+    M, N, K = 300, 768, 2048
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    need = m.nvfp4_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+
+    def offset_copy(arr, off):
+        buf = torch.zeros(arr.size + 64, dtype=torch.uint8, device=dev)
+        view = buf[off:off + arr.size].view(arr.shape)
+        view.copy_(torch.from_numpy(np.ascontiguousarray(arr)))
+        return view
+
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    m.nvfp4_gemm_ws(to_dev(qa), offset_copy(sfa, 4), to_dev(np.array([sa], np.float32)), M, qa.shape[0], to_dev(qw),
+                    offset_copy(sfw, 4), to_dev(np.array([sw], np.float32)), N, K, out, N, ws, need)
+    torch.cuda.synchronize()
+    check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), out_f64(out), "ws misaligned scales")

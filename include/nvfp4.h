@@ -91,9 +91,13 @@ typedef struct {
  * "FC2 NVFP4 Library Scheduling", Exact Operation). */
 int64_t nvfp4_padded_rows(int64_t m);
 
-/* Bytes of device workspace the absmax passes need.  The workspace must be
- * zero-filled once before its first use; every completed absmax call leaves
- * it zero-filled again.  It must not be shared by calls that may overlap. */
+/* Bytes of device workspace the absmax passes and nvfp4_modulate_quantize
+ * need (8,448: the global maximum and a counter of the two-pass kernels, and
+ * the single launch's generation word, result word and one arrival word per
+ * workgroup).  The workspace must be zero-filled before its first use; after
+ * that any sequence of calls may reuse it without clearing (the two-pass
+ * kernels return their words to zero, the single launch tags its words with
+ * a generation count).  It must not be shared by calls that may overlap. */
 size_t nvfp4_absmax_workspace_bytes(void);
 
 /* Pass 1 of the modulation producer ("NVFP4 Modulation Producer Fusion",
@@ -118,6 +122,27 @@ nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int6
 nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                                  const nvfp4_segments* seg, const float* tensor_scale,
                                  uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);
+
+/* Both passes of the modulation producer in one launch (same results as
+ * nvfp4_modulate_absmax followed by nvfp4_modulate_pack, byte for byte).  The
+ * workgroups (at most as many as the device holds at once) run pass 1, meet
+ * at a grid barrier once the global maximum is complete ("NVFP4 Streaming
+ * Design", Numerical Constraint: no block is packed before the global
+ * reduction, and the two phases may be joined around a grid-wide barrier),
+ * and run pass 2, which takes the y of
+ * the rows each workgroup visited last from registers and LDS instead of
+ * reading x again.  Writes *tensor_scale, *amax_out (may be NULL), qdata and
+ * sfa as the two calls do; uses the same workspace.  The barrier needs every
+ * workgroup resident; if kernels on other streams keep compute units occupied
+ * so long that its wait passes 1 s, the call completes with a NaN tensor
+ * scale and amax, scale code 0x7F and zero codes in every block, and so does
+ * every later single-launch call on that workspace until it is zero-filled
+ * again.  When D > 16384 it enqueues the two passes instead.  Same
+ * requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack together. */
+nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                     const nvfp4_segments* seg, void* workspace, float* tensor_scale,
+                                     float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
+                                     void* stream);
 
 /* Pass 1 of the SwiGLU producer ("FC2 NVFP4 Library Scheduling", Exact
  * Operation and Current Baseline: exact BF16 SwiGLU fused into NVFP4

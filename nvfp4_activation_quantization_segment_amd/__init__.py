@@ -51,6 +51,7 @@ def _load():
         "nvfp4_absmax_workspace_bytes": (ctypes.c_size_t, []),
         "nvfp4_modulate_absmax": (I32, [P, I64, I64, I64, SEG, P, P, P, V]),
         "nvfp4_modulate_pack": (I32, [P, I64, I64, I64, SEG, P, P, P, I64, V]),
+        "nvfp4_modulate_quantize": (I32, [P, I64, I64, I64, SEG, P, P, P, P, P, I64, V]),
         "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
         "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
         "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
@@ -150,6 +151,12 @@ def nvfp4_modulate_pack(x, M, D, ldx, seg, tensor_scale, qdata, sfa, M_pad, stre
                                    _ptr(sfa), M_pad, _stream(stream)))
 
 
+def nvfp4_modulate_quantize(x, M, D, ldx, seg, ws, tensor_scale, amax_out, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_modulate_quantize",
+           lib.nvfp4_modulate_quantize(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(ws), _ptr(tensor_scale),
+                                       _ptr(amax_out), _ptr(qdata), _ptr(sfa), M_pad, _stream(stream)))
+
+
 def nvfp4_swiglu_absmax(gate, up, M, F, ld, ws, tensor_scale, amax_out=None, stream=None):
     _check("nvfp4_swiglu_absmax",
            lib.nvfp4_swiglu_absmax(_ptr(gate), _ptr(up), M, F, ld, _ptr(ws), _ptr(tensor_scale), _ptr(amax_out),
@@ -209,8 +216,11 @@ def nvfp4_step_e4m3(t, code, n, stream=None):
 # conveniences (torch allocates the outputs)
 # ---------------------------------------------------------------------------
 def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: torch.Tensor, m_pad: int | None = None,
-                      stream=None):
-    """x [M, D] bf16 -> (qdata [M_pad, D/2] u8, sfa [M_pad, D/16] u8, tensor_scale f32[1], amax f32[1])."""
+                      stream=None, single_pass: bool = True):
+    """x [M, D] bf16 -> (qdata [M_pad, D/2] u8, sfa [M_pad, D/16] u8, tensor_scale f32[1], amax f32[1]).
+
+    single_pass: one nvfp4_modulate_quantize launch; else nvfp4_modulate_absmax
+    then nvfp4_modulate_pack (identical bytes)."""
     _bits16(x)
     M, D = x.shape
     if x.stride(1) != 1:
@@ -222,8 +232,11 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
     amax = torch.empty(1, dtype=torch.float32, device=dev)
     q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
-    nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, stream)
-    nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, stream)
+    if single_pass:
+        nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, q, s, m_pad, stream)
+    else:
+        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, stream)
+        nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, stream)
     del keep
     return q, s, ts, amax
 

@@ -90,7 +90,7 @@ extern "C" {
 
 int64_t nvfp4_padded_rows(int64_t m) { return m <= 0 ? 0 : pad64(m); }
 
-size_t nvfp4_absmax_workspace_bytes(void) { return 256; }
+size_t nvfp4_absmax_workspace_bytes(void) { return kWorkspaceBytes; }
 
 const char* nvfp4_status_string(nvfp4_status s) {
     switch (s) {
@@ -132,6 +132,32 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     const RowGeo g = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
     return hip_status(launch_modulate_pack(x, g, sp, tensor_scale, qdata, sfa, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                     const nvfp4_segments* seg, void* workspace, float* tensor_scale,
+                                     float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream) {
+    nvfp4_status st = check_rows(x, M, D, ldx);
+    if (st != NVFP4_OK) return st;
+    SegParams sp;
+    if ((st = check_segments(seg, M, D, &sp)) != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    // one cooperative launch when a row fits one workgroup (D <= 16384)
+    const int G = D / 16 <= 1024 ? modulate_quantize_grid() : 0;
+    if (G > 0) {
+        const RowGeo g = row_geo(M, M_pad, D, ldx, G, 1, 16);
+        return hip_status(launch_modulate_quantize(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, qdata,
+                                                   sfa, s));
+    }
+    const RowGeo g1 = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
+    if ((st = hip_status(launch_modulate_absmax(x, g1, sp, (uint32_t*)workspace, tensor_scale, amax_out, s))) !=
+        NVFP4_OK)
+        return st;
+    const RowGeo g2 = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
+    return hip_status(launch_modulate_pack(x, g2, sp, tensor_scale, qdata, sfa, s));
 }
 
 nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,

@@ -39,6 +39,16 @@ hipError_t launch_modulate_absmax(const uint16_t* x, const RowGeo& g, const SegP
                                   float* tensor_scale, float* amax_out, hipStream_t s);
 hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegParams& seg, const float* tensor_scale,
                                 uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+// Single-pass producer: one launch of at most modulate_quantize_grid()
+// workgroups, all resident at once (0 when that cannot be determined).  The
+// workspace holds one 8-byte arrival word per workgroup after 256 header bytes.
+constexpr int kMaxDevices = 32;
+constexpr int kMaxGridSlots = 1024;
+constexpr size_t kWorkspaceBytes = 256 + 8 * kMaxGridSlots;
+int modulate_quantize_grid();
+hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
+                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                    hipStream_t s);
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, hipStream_t s);
 hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,

@@ -353,6 +353,439 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Single-pass producer
+//
+// One launch does both passes.  Every workgroup runs pass 1 over its row
+// groups, the workgroups meet at a grid barrier where the global maximum is
+// complete, and pass 2 follows in the same launch.  The y values of the row
+// groups a workgroup visited last stay on chip across the barrier: the last
+// kHoldRegs groups in registers, the ones before them in LDS; pass 2 packs
+// those first and then reads only the remaining rows from memory again, last
+// to first.  The grid never exceeds the workgroups the device holds at once
+// (one per CU: the held rows fill the LDS), so the barrier completes on a
+// device that other streams do not keep occupied; its wait is bounded in any
+// case (see grid_max_barrier).
+//
+// Thread layout as in the pack passes: thread idx takes block idx % C16 of row
+// offset idx / C16 in a group of R rows; workgroup w visits groups w, w+G, ...
+// ---------------------------------------------------------------------------
+constexpr int kHoldRegs = 7;                 // row groups held in registers per thread
+constexpr int kModHoldLdsBytes = 152 * 1024;  // LDS for held groups (modulation)
+constexpr uint64_t kBarrierTicks = 100000000;  // wait bound: 1 s of the 100 MHz real-time counter
+
+// Column parameters of one 16-column block as bf16 pairs: bf16(scale+1) and
+// shift of columns 2j (low half) and 2j+1 (high half).
+struct ColPk {
+    uint32_t s1[8];
+    uint32_t sh[8];
+};
+
+__device__ __forceinline__ void load_cols_pk(const SegParams& seg, int s, int b, ColPk& cp) {
+    const uint16_t* sc = seg.scale + (int64_t)s * seg.ld + 16 * b;
+    const uint16_t* sh = seg.shift + (int64_t)s * seg.ld + 16 * b;
+    const uint4 c0 = ld16(sc), c1 = ld16(sc + 8), h0 = ld16(sh), h1 = ld16(sh + 8);
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float a = __uint_as_float(cw[j] << 16) + 1.0f;
+        const float c = __uint_as_float(cw[j] & 0xFFFF0000u) + 1.0f;
+        cp.s1[j] = pack_bf16x2(a, c);
+        cp.sh[j] = hw[j];
+    }
+}
+
+// y for 16 consecutive columns: xw = the 8 words of x, y = 8 words of y.
+__device__ __forceinline__ void modulate16_pk(const uint32_t xw[8], const ColPk& cp, uint32_t y[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t p = pack_bf16x2(bf16_lo(xw[j]) * bf16_lo(cp.s1[j]), bf16_hi(xw[j]) * bf16_hi(cp.s1[j]));
+        y[j] = pack_bf16x2(bf16_lo(p) + bf16_lo(cp.sh[j]), bf16_hi(p) + bf16_hi(cp.sh[j]));
+    }
+}
+
+__device__ __forceinline__ void ld32(const uint16_t* p, uint32_t w[8]) {
+    const uint4 a = ld16(p), c = ld16(p + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
+}
+
+__device__ __forceinline__ void max16(uint32_t& m2, const uint32_t y[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
+}
+
+// Segment of row r starting from segment s (rows may move either way).
+__device__ __forceinline__ int seg_find(const SegParams& seg, int64_t r, int s) {
+    while (r >= seg.row_start[s + 1]) ++s;
+    while (r < seg.row_start[s]) --s;
+    return s;
+}
+
+// Workgroup maximum, then the grid barrier of the single launch.
+//
+// Workspace layout: 32-bit words 0 and 1 belong to the two-pass absmax
+// kernels; the single launch uses a generation word (64-bit, byte 64), a
+// result word (64-bit, byte 128) and one arrival word per workgroup (64-bit,
+// from byte 256).  Result and arrival words carry a 44-bit generation tag
+// above a 20-bit payload.  A call reads the generation e at its start and
+// works with tag e+1:
+//  - arrival: each workgroup stores (e+1, its maximum) into its own word, so
+//    no two workgroups contend for one word (same-address atomics serialize
+//    at ~0.1 us each, which made a counter-based barrier cost 20 us);
+//  - workgroup 0 polls every arrival word until all carry tag e+1, forms the
+//    maximum, publishes (e+1, published, bits) into the result word with a
+//    compare-and-swap, then stores generation e+1 for the next call;
+//  - the other workgroups poll the result word for tag e+1.
+// Nothing is ever reset: stale words carry older tags.  A wait that runs past
+// the bound ends in an abandon, also by compare-and-swap on the result word,
+// so exactly one outcome is visible to every workgroup: the true maximum, or
+// NaN.  An abandon does not advance the generation, so later calls on the
+// workspace find the abandoned result of their tag and also yield NaN, until
+// the caller zero-fills the workspace again.
+constexpr int kGenQword = 8;       // 64-bit word index (byte 64)
+constexpr int kResultQword = 16;   // 64-bit word index (byte 128)
+constexpr int kSlotQword = 32;     // 64-bit word index of workgroup 0's arrival word (byte 256)
+constexpr uint32_t kPublished = 0x10000u, kAbandoned = 0x20000u;
+constexpr uint32_t kNanBits = 0x7FC0u;
+
+__device__ __forceinline__ uint64_t load_dev64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cas_dev64(uint64_t* p, uint64_t expect, uint64_t v) {
+    __hip_atomic_compare_exchange_strong(p, &expect, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return expect;  // the value found
+}
+__device__ __forceinline__ uint64_t tag_of(uint64_t w) { return w >> 20; }
+__device__ __forceinline__ uint64_t tagged(uint64_t tag, uint32_t v) { return (tag << 20) | v; }
+
+__device__ __forceinline__ void write_scale(uint32_t bits, float* tensor_scale, float* amax_out) {
+    const float amax = __uint_as_float(bits << 16);
+    tensor_scale[0] = (amax == 0.0f) ? 1.0f : amax / 2688.0f;
+    if (amax_out) amax_out[0] = amax;
+}
+
+// Result word -> magnitude bits (NaN for an abandoned barrier).
+__device__ __forceinline__ uint32_t outcome_bits(uint64_t r) {
+    return ((uint32_t)r & kAbandoned) ? kNanBits : ((uint32_t)r & 0xFFFFu);
+}
+
+// Settles the result word of tag `tag`: installs `want` unless a word of this
+// tag is already there; returns the word that holds.
+__device__ __forceinline__ uint64_t settle(uint64_t* res, uint64_t tag, uint64_t want) {
+    uint64_t cur = load_dev64(res);
+    while (tag_of(cur) != tag) {
+        const uint64_t found = cas_dev64(res, cur, want);
+        if (found == cur) return want;
+        cur = found;
+    }
+    return cur;
+}
+
+// The generation this call works under, read once by thread 0 at the start.
+__device__ __forceinline__ uint64_t grid_generation(const uint32_t* ws) {
+    return threadIdx.x == 0 ? load_dev64(reinterpret_cast<const uint64_t*>(ws) + kGenQword) : 0u;
+}
+
+__device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, uint64_t gen, float* tensor_scale,
+                                     float* amax_out) {
+    __shared__ uint32_t red[16];
+    __shared__ uint32_t result;
+    __shared__ uint64_t tag_s;
+    uint64_t* q = reinterpret_cast<uint64_t*>(ws);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int nwv = (blockDim.x + 63) >> 6;
+    m16 = wave_max_u32(m16);
+    if (lane == 0) red[wv] = m16;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t mm = 0;
+        for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
+        tag_s = gen + 1u;
+        store_dev64(&q[kSlotQword + blockIdx.x], tagged(gen + 1u, mm));
+    }
+    if (blockIdx.x == 0) {
+        __syncthreads();
+        const uint64_t tag = tag_s;
+        // every thread polls its share of the arrival words
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        uint32_t mine = 0;
+        int next = threadIdx.x;
+        bool late = false;  // uniform over the workgroup
+        for (;;) {
+            while (next < (int)gridDim.x) {
+                const uint64_t v = load_dev64(&q[kSlotQword + next]);
+                if (tag_of(v) != tag) break;
+                mine = ((uint32_t)v & 0xFFFFu) > mine ? ((uint32_t)v & 0xFFFFu) : mine;
+                next += blockDim.x;
+            }
+            if (__syncthreads_and(next >= (int)gridDim.x)) break;
+            if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks)) {
+                late = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        mine = wave_max_u32(mine);
+        __syncthreads();
+        if (lane == 0) red[wv] = mine;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t mm = 0;
+            for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
+            const uint64_t want = tagged(tag, late ? kAbandoned : (kPublished | mm));
+            const uint64_t r = settle(&q[kResultQword], tag, want);
+            if (r == want) {
+                write_scale(outcome_bits(r), tensor_scale, amax_out);
+                if (!late) store_dev64(&q[kGenQword], tag);
+            }
+            result = outcome_bits(r);
+        }
+    } else if (threadIdx.x == 0) {
+        const uint64_t tag = gen + 1u;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        uint64_t r;
+        while (tag_of(r = load_dev64(&q[kResultQword])) != tag) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
+                const uint64_t want = tagged(tag, kAbandoned);
+                r = settle(&q[kResultQword], tag, want);
+                if (r == want) write_scale(kNanBits, tensor_scale, amax_out);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        result = outcome_bits(r);
+    }
+    __syncthreads();
+    return result;
+}
+
+// Per-workgroup split of its nw row groups: ns streamed (re-read in pass 2),
+// nl held in LDS, nr held in registers (the last ones visited).  Only the very
+// last group of the tensor can be partial, and it is register-held.
+struct HoldSplit {
+    int ns, nl, nr;
+};
+__device__ __forceinline__ HoldSplit hold_split(int64_t groups, int hold_lds) {
+    const int64_t G = gridDim.x, w = blockIdx.x;
+    const int nw = w < groups ? (int)((groups - 1 - w) / G + 1) : 0;
+    HoldSplit h;
+    h.nr = nw < kHoldRegs ? nw : kHoldRegs;
+    h.nl = (nw - h.nr) < hold_lds ? (nw - h.nr) : hold_lds;
+    h.ns = nw - h.nr - h.nl;
+    return h;
+}
+
+// LDS slot of held group h for thread idx: [h][half][idx] in 16-byte words.
+__device__ __forceinline__ void hold_put(uint4* hold, int h, const uint32_t y[8]) {
+    hold[(2 * h) * blockDim.x + threadIdx.x] = make_uint4(y[0], y[1], y[2], y[3]);
+    hold[(2 * h + 1) * blockDim.x + threadIdx.x] = make_uint4(y[4], y[5], y[6], y[7]);
+}
+__device__ __forceinline__ void hold_get(const uint4* hold, int h, uint32_t y[8]) {
+    const uint4 a = hold[(2 * h) * blockDim.x + threadIdx.x];
+    const uint4 c = hold[(2 * h + 1) * blockDim.x + threadIdx.x];
+    y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
+    y[4] = c.x; y[5] = c.y; y[6] = c.z; y[7] = c.w;
+}
+
+__device__ __forceinline__ void zero_pad_rows(const RowGeo& g, uint8_t* qdata, uint8_t* sfa) {
+    const int C16 = g.C8 >> 1;
+    const int64_t n = (g.rows_total - g.M) * C16;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = g.M + i / C16;
+        const int b = (int)(i % C16);
+        *reinterpret_cast<uint2*>(qdata + r * 8 * C16 + 8 * b) = make_uint2(0u, 0u);
+        sfa[r * C16 + b] = 0;
+    }
+}
+
+// Pass 2 of the single launch: register-held groups, then LDS-held ones,
+// then the streamed groups last to first, whose column parameters are loaded
+// afresh (nothing of pass 1 stays live across the held groups).  Every thread
+// of the workgroup runs the loops (`on` guards the memory accesses) so that
+// the streamed loop can end each iteration with a workgroup barrier: left to
+// themselves the waves of a workgroup drift apart by ~30 us over this loop
+// (the first waves win the memory queue), and the last ones then finish alone
+// with too few loads in flight.
+__device__ __forceinline__ void pass2_mod(const uint16_t* __restrict__ x, const RowGeo& g, const SegParams& seg,
+                                          const uint32_t (&hy)[kHoldRegs][8], const uint4* hold, const HoldSplit& hs,
+                                          const float2* dr, float s_g, float rg, bool sg_fast, bool on,
+                                          int64_t r_first, int64_t gstride, int b, uint8_t* __restrict__ qdata,
+                                          uint8_t* __restrict__ sfa) {
+    const int C16 = g.C8 >> 1;
+    const int64_t qld = 8 * (int64_t)C16, sld = C16;
+    const int t0 = hs.ns + hs.nl;
+    if (on) {
+#pragma unroll
+        for (int h = 0; h < kHoldRegs; ++h) {
+            const int64_t r = r_first + (t0 + h) * gstride;
+            if (h < hs.nr && r < g.M)
+                pack_block16_store(hy[h], s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+        }
+        for (int h = hs.nl - 1; h >= 0; --h) {
+            const int64_t r = r_first + (hs.ns + h) * gstride;
+            uint32_t y[8];
+            hold_get(hold, h, y);
+            pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+        }
+    }
+    int t = hs.ns - 1;
+    if (t < 0) return;  // uniform over the workgroup
+    int s2 = 0;
+    ColParams c0, c1;  // binary32 parameters: the streamed loop is short of VALU, not of registers
+    int64_t seg_lo = 0;  // rows decrease in this loop
+    if (on) {
+        s2 = seg_find(seg, r_first + t * gstride, 0);
+        load_cols(seg, s2, 2 * b, c0);
+        load_cols(seg, s2, 2 * b + 1, c1);
+        seg_lo = seg.row_start[s2];
+    }
+    auto pack = [&](const uint4& v0, const uint4& v1, int64_t r) {
+        if (r < seg_lo) {
+            s2 = seg_find(seg, r, s2);
+            seg_lo = seg.row_start[s2];
+            load_cols(seg, s2, 2 * b, c0);
+            load_cols(seg, s2, 2 * b + 1, c1);
+        }
+        uint32_t y[8];
+        modulate8(v0, c0, y);
+        modulate8(v1, c1, y + 4);
+        pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+    };
+    for (; t >= 1; t -= 2) {
+        if (on) {
+            const int64_t r0 = r_first + t * gstride, r1 = r0 - gstride;
+            const uint16_t* p0 = x + r0 * g.ldx + 16 * b;
+            const uint16_t* p1 = x + r1 * g.ldx + 16 * b;
+            const uint4 a0 = ld16(p0), a1 = ld16(p0 + 8), b0 = ld16(p1), b1 = ld16(p1 + 8);
+            pack(a0, a1, r0);
+            pack(b0, b1, r1);
+        }
+        __syncthreads();
+    }
+    if (t == 0 && on) {
+        const uint16_t* p0 = x + r_first * g.ldx + 16 * b;
+        pack(ld16(p0), ld16(p0 + 8), r_first);
+    }
+}
+
+__global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t* __restrict__ x, RowGeo g,
+                                                                 SegParams seg, uint32_t* ws, float* tensor_scale,
+                                                                 float* amax_out, uint8_t* __restrict__ qdata,
+                                                                 uint8_t* __restrict__ sfa, int hold_lds) {
+    __shared__ uint4 hold[kModHoldLdsBytes / 16];
+    __shared__ float2 dr[128];
+    const int C16 = g.C8 >> 1;
+    const int rho = threadIdx.x / C16, b = threadIdx.x - rho * C16;
+    const bool on = rho < g.R;
+    const int64_t groups = (g.M + g.R - 1) / g.R;
+    const HoldSplit hs = hold_split(groups, hold_lds);
+    const int64_t gstride = (int64_t)gridDim.x * g.R;
+    const int64_t r_first = (int64_t)blockIdx.x * g.R + rho;  // row of local group 0
+    const uint64_t gen = grid_generation(ws);
+
+    // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
+    uint32_t m2 = 0;
+    uint32_t hy[kHoldRegs][8];
+    // held groups: packed column parameters, loaded at their first row
+    int s = 0;
+    ColPk cp;
+    int64_t seg_hi = 0;  // rows increase in pass 1
+    // Streamed groups, two per iteration, with binary32 column parameters
+    // (short of VALU here, not of registers: the held groups come later).
+    int t = 0;
+    {
+        ColParams c0, c1;
+        int64_t hi = 0;
+        int sc = 0;
+        if (on) {
+            sc = seg_find(seg, r_first < g.M ? r_first : 0, 0);
+            load_cols(seg, sc, 2 * b, c0);
+            load_cols(seg, sc, 2 * b + 1, c1);
+            hi = seg.row_start[sc + 1];
+        }
+        auto absmax = [&](const uint4& v0, const uint4& v1, int64_t r) {
+            if (r >= hi) {
+                sc = seg_find(seg, r, sc);
+                hi = seg.row_start[sc + 1];
+                load_cols(seg, sc, 2 * b, c0);
+                load_cols(seg, sc, 2 * b + 1, c1);
+            }
+            uint32_t y[8];
+            modulate8(v0, c0, y);
+            modulate8(v1, c1, y + 4);
+            max16(m2, y);
+        };
+        for (; t + 1 < hs.ns; t += 2) {
+            if (on) {
+                const int64_t r0 = r_first + t * gstride, r1 = r0 + gstride;
+                const uint16_t* p0 = x + r0 * g.ldx + 16 * b;
+                const uint16_t* p1 = x + r1 * g.ldx + 16 * b;
+                const uint4 a0 = ld16(p0), a1 = ld16(p0 + 8), b0 = ld16(p1), b1 = ld16(p1 + 8);
+                absmax(a0, a1, r0);
+                absmax(b0, b1, r1);
+            }
+        }
+    }
+    if (on) {
+        for (; t < hs.ns + hs.nl; ++t) {
+            const int64_t r = r_first + t * gstride;
+            uint32_t v[8], y[8];
+            ld32(x + r * g.ldx + 16 * b, v);
+            if (r >= seg_hi) {
+                s = seg_find(seg, r, s);
+                seg_hi = seg.row_start[s + 1];
+                load_cols_pk(seg, s, b, cp);
+            }
+            modulate16_pk(v, cp, y);
+            max16(m2, y);
+            if (t >= hs.ns) hold_put(hold, t - hs.ns, y);
+        }
+        // register-held groups: all loads first, then y in place of x
+        const int t0 = hs.ns + hs.nl;
+#pragma unroll
+        for (int h = 0; h < kHoldRegs; ++h) {
+            const int64_t r = r_first + (t0 + h) * gstride;
+            if (h < hs.nr && r < g.M) {
+                ld32(x + r * g.ldx + 16 * b, hy[h]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) hy[h][k] = 0u;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kHoldRegs; ++h) {
+            const int64_t r = r_first + (t0 + h) * gstride;
+            const bool valid = h < hs.nr && r < g.M;
+            if (valid && r >= seg_hi) {
+                s = seg_find(seg, r, s);
+                seg_hi = seg.row_start[s + 1];
+                load_cols_pk(seg, s, b, cp);
+            }
+            uint32_t y[8];
+            modulate16_pk(hy[h], cp, y);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) hy[h][k] = y[k];
+            if (valid) max16(m2, y);
+        }
+    }
+    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, gen, tensor_scale, amax_out);
+
+    // ---- pass 2 ----
+    const float amax = __uint_as_float(bits << 16);
+    const float s_g = (amax == 0.0f) ? 1.0f : amax / 2688.0f;
+    build_dr_table(dr, s_g);
+    const bool sg_fast = scale_in_fast_range(s_g);
+    const float rg = 1.0f / s_g;
+    zero_pad_rows(g, qdata, sfa);
+    pass2_mod(x, g, seg, hy, hold, hs, dr, s_g, rg, sg_fast, on, r_first, gstride, b, qdata, sfa);
+}
+
+// ---------------------------------------------------------------------------
 // Single-step kernels (elementwise, grid-stride)
 // ---------------------------------------------------------------------------
 __global__ void step_modulate_kernel(const uint16_t* x, const uint16_t* sc, const uint16_t* sh, uint16_t* y,
@@ -433,6 +866,47 @@ hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegPar
                                 uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
     hipLaunchKernelGGL(modulate_pack_kernel, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, tensor_scale, qdata, sfa,
                        g.reverse);
+    return hipGetLastError();
+}
+
+// Workgroups of the single-launch kernel that the current device holds at
+// once (occupancy of a 1024-thread workgroup, which bounds every smaller one,
+// times the CU count), capped at the workspace's arrival words; cached per
+// device.  0 when it cannot be determined.
+static int resident_grid(const void* kernel, int* cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (cache[dev] >= 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 1024, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int n = cus * per_cu;
+    cache[dev] = n < kMaxGridSlots ? n : kMaxGridSlots;
+    return cache[dev];
+}
+
+int modulate_quantize_grid() {
+    static int cache[kMaxDevices] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
+                                     -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+    return resident_grid((const void*)modulate_quantize_kernel, cache);
+}
+
+// A plain launch: the grid never exceeds what the device holds at once, so on
+// a device not kept busy by other streams every workgroup is resident and the
+// barrier completes (its wait is bounded in any case).  The cooperative launch
+// API would guarantee residency but costs tens of microseconds per launch.
+hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
+                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                    hipStream_t s) {
+    const int hold_lds = kModHoldLdsBytes / (32 * g.block);
+    hipLaunchKernelGGL(modulate_quantize_kernel, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws, tensor_scale,
+                       amax_out, qdata, sfa, hold_lds);
     return hipGetLastError();
 }
 

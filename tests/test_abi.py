@@ -112,6 +112,14 @@ def test_producer_argument_errors(pkg):
     assert L.nvfp4_modulate_absmax(FAKE, 17, 64, 64, ctypes.byref(many), ws, ts, None, None) == 4
     assert L.nvfp4_modulate_pack(FAKE, 10, 64, 64, ctypes.byref(seg), ts, q, s, 32, None) == 2     # M_pad
     assert L.nvfp4_modulate_pack(FAKE, 10, 64, 64, ctypes.byref(seg), ts, q + 1, s, 64, None) == 3
+    mq = L.nvfp4_modulate_quantize
+    assert mq(None, 10, 64, 64, ctypes.byref(seg), ws, ts, None, q, s, 64, None) == 1
+    assert mq(FAKE, 10, 40, 40, ctypes.byref(seg), ws, ts, None, q, s, 64, None) == 2            # D % 16
+    assert mq(FAKE, 10, 64, 64, ctypes.byref(bad), ws, ts, None, q, s, 64, None) == 4            # segments
+    assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), None, ts, None, q, s, 64, None) == 1          # workspace
+    assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, None, q, s, 32, None) == 2            # M_pad
+    assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, None, q + 1, s, 64, None) == 3        # qdata
+    assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, FAKE + 2, q, s, 64, None) == 3        # amax_out
     assert L.nvfp4_swiglu_absmax(FAKE, FAKE, 10, 24, 48, ws, ts, None, None) == 2
     assert L.nvfp4_swiglu_pack(FAKE, None, 10, 32, 64, ts, q, s, 64, None) == 1
 

@@ -23,8 +23,9 @@ def m():
     return pkg
 
 
-def gpu_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None):
-    """Run both passes on the GPU; x may be given with a wider row stride."""
+def gpu_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None, single_pass=False):
+    """Run the producer on the GPU (the two pass entry points, or the single
+    launch); x may be given with a wider row stride."""
     M, D = x.shape
     if ldx is not None and ldx != D:
         wide = np.zeros((M, ldx), np.uint16)
@@ -32,7 +33,8 @@ def gpu_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None):
         xd = to_dev_u16(wide)[:, :D]
     else:
         xd = to_dev_u16(x)
-    q, s, ts, amax = m.modulate_quantize(xd, row_start, to_dev_u16(shift), to_dev_u16(scale), m_pad=m_pad)
+    q, s, ts, amax = m.modulate_quantize(xd, row_start, to_dev_u16(shift), to_dev_u16(scale), m_pad=m_pad,
+                                         single_pass=single_pass)
     torch.cuda.synchronize()
     return host(ts)[0], host(q), host(s), host(amax)[0]
 
@@ -42,11 +44,13 @@ def check_modulate(m, x, row_start, shift, scale, m_pad=None, ldx=None):
     m_pad = oracle.padded_rows(M) if m_pad is None else m_pad
     seg = oracle.Segments(row_start, shift, scale)
     s_g, q, s, amax = _par.modulate_quantize(x, seg, m_pad)
-    gs, gq, gsf, gamax = gpu_modulate(m, x, row_start, shift, scale, m_pad, ldx)
-    assert np.float32(gamax).view(np.uint32) == np.float32(amax).view(np.uint32), (gamax, amax)
-    assert np.float32(gs).view(np.uint32) == np.float32(s_g).view(np.uint32), (gs, s_g)
-    assert np.array_equal(gsf, s), "SFA " + str(first_mismatch(gsf, s))
-    assert np.array_equal(gq, q), "QDATA " + str(first_mismatch(gq, q))
+    for single in (False, True):
+        gs, gq, gsf, gamax = gpu_modulate(m, x, row_start, shift, scale, m_pad, ldx, single)
+        path = "single launch" if single else "two passes"
+        assert np.float32(gamax).view(np.uint32) == np.float32(amax).view(np.uint32), (path, gamax, amax)
+        assert np.float32(gs).view(np.uint32) == np.float32(s_g).view(np.uint32), (path, gs, s_g)
+        assert np.array_equal(gsf, s), path + ": SFA " + str(first_mismatch(gsf, s))
+        assert np.array_equal(gq, q), path + ": QDATA " + str(first_mismatch(gq, q))
     return s_g
 
 
@@ -78,6 +82,8 @@ def test_tiny_workload_byte_exact(m):
     (97, 5376, (0, 31, 97), 5392),            # strided rows
     (300, 256, tuple(range(0, 300, 20)) + (300,), None),   # 15 segments
     (40, 64, tuple(range(0, 16)) + (40,), None),            # 16 segments (the maximum)
+    (21, 16400, (0, 5, 21), None),          # 1025 blocks per row: the single launch runs the two passes
+    (769, 5376, (0, 500, 769), None),       # three-row groups, the last one partial
 ])
 def test_ragged_shapes_and_segments(m, M, D, segs, ldx):
     rng = np.random.default_rng(M * 7 + D)
@@ -143,21 +149,37 @@ def test_tiny_global_maximum_uses_exact_division(m):
     check_values(m, y)
 
 
-def test_workspace_resets_between_calls(m):
-    """Two absmax calls in a row on one workspace: the second sees only its own
-    tensor (a smaller maximum), and the workspace returns to zero."""
+def test_workspace_reuse_between_calls(m):
+    """Calls in a row on one workspace, alternating the single launch and the
+    two passes: each sees only its own tensor (the maxima differ).  The two
+    passes leave their words at zero; the single launch tags its words with a
+    generation count, which advances by one per call."""
     dev = device()
     rs = [0, 64]
     sh = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
     sc = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
-    big = torch.full((64, 64), 100.0, dtype=torch.bfloat16, device=dev)
-    small = torch.full((64, 64), 2.0, dtype=torch.bfloat16, device=dev)
-    _, _, ts1, a1 = m.modulate_quantize(big, rs, sh, sc)
-    _, _, ts2, a2 = m.modulate_quantize(small, rs, sh, sc)
-    torch.cuda.synchronize()
-    assert host(a1)[0] == 100.0 and host(a2)[0] == 2.0
-    assert host(ts2)[0] == np.float32(2.0) / np.float32(2688.0)
-    assert not host(m.workspace(dev)).any()
+    ws = torch.zeros(int(m.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
+    gen = 0
+    for single in (True, False, True, True):
+        for val in (100.0, 2.0, 37.0):
+            t = torch.full((64, 64), val, dtype=torch.bfloat16, device=dev)
+            seg, keep = m.make_segments(rs, sh, sc)
+            ts = torch.empty(1, dtype=torch.float32, device=dev)
+            a = torch.empty(1, dtype=torch.float32, device=dev)
+            q = torch.empty((64, 32), dtype=torch.uint8, device=dev)
+            s = torch.empty((64, 4), dtype=torch.uint8, device=dev)
+            if single:
+                m.nvfp4_modulate_quantize(t, 64, 64, 64, seg, ws, ts, a, q, s, 64)
+                gen += 1
+            else:
+                m.nvfp4_modulate_absmax(t, 64, 64, 64, seg, ws, ts, a)
+                m.nvfp4_modulate_pack(t, 64, 64, 64, seg, ts, q, s, 64)
+            torch.cuda.synchronize()
+            assert host(a)[0] == val
+            assert host(ts)[0] == np.float32(val) / np.float32(2688.0)
+            w = host(ws)
+            assert not w[:8].any()
+            assert int(w[64:72].view(np.uint64)[0]) == gen
 
 
 def test_non_default_stream(m):
@@ -169,11 +191,47 @@ def test_non_default_stream(m):
     st = torch.cuda.Stream()
     xd, shd, scd = to_dev_u16(x), to_dev_u16(sh), to_dev_u16(sc)
     torch.cuda.synchronize()
-    with torch.cuda.stream(st):
-        gq, gs, gts, _ = m.modulate_quantize(xd, rs, shd, scd, stream=st)
-    st.synchronize()
-    assert np.array_equal(host(gq), q) and np.array_equal(host(gs), s)
-    assert host(gts)[0] == s_g
+    for single in (False, True):
+        with torch.cuda.stream(st):
+            gq, gs, gts, _ = m.modulate_quantize(xd, rs, shd, scd, stream=st, single_pass=single)
+        st.synchronize()
+        assert np.array_equal(host(gq), q) and np.array_equal(host(gs), s)
+        assert host(gts)[0] == s_g
+
+
+def test_single_launch_without_amax_output(m):
+    """nvfp4_modulate_quantize with amax_out = NULL writes the same bytes."""
+    w = synth.workload("tiny")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    s_g, q, s, _ = oracle.modulate_quantize(x, oracle.Segments(rs, sh, sc))
+    dev = device()
+    seg, keep = m.make_segments(rs, to_dev_u16(sh), to_dev_u16(sc))
+    xd = to_dev_u16(x)
+    mp = oracle.padded_rows(w.M)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    qd = torch.full((mp, w.K // 2), 0xAB, dtype=torch.uint8, device=dev)
+    sd = torch.full((mp, w.K // 16), 0xAB, dtype=torch.uint8, device=dev)
+    m.nvfp4_modulate_quantize(xd, w.M, w.K, w.K, seg, m.workspace(dev), ts, None, qd, sd, mp)
+    torch.cuda.synchronize()
+    assert host(ts)[0] == s_g and np.array_equal(host(qd), q) and np.array_equal(host(sd), s)
+    del keep
+
+
+def test_single_launch_streams_and_holds_rows(m):
+    """A tensor large enough that every workgroup of the single launch streams
+    rows again in its second pass, besides the rows it holds in registers and
+    LDS (60,000 x 1,024), with 16 segments whose boundaries the reversed second
+    pass crosses."""
+    rng = np.random.default_rng(77)
+    M, D = 60000, 1024
+    x = bf16_np(rng.standard_normal((M, D)) * np.where(rng.random((M, D)) < 0.001, 50.0, 1.0))
+    segs = np.array([0, 1, 17, 1000, 4095, 4096, 9000, 15000, 22222, 30000, 30001, 41000, 50000, 55555, 59000,
+                     59999, 60000], np.int64)
+    S = segs.size - 1
+    sh = bf16_np(0.1 * rng.standard_normal((S, D)))
+    sc = bf16_np(0.1 * rng.standard_normal((S, D)))
+    check_modulate(m, x, segs, sh, sc)
 
 
 def test_weight_prepack_matches_oracle_quantizer(m):

@@ -22,6 +22,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
+// Streaming stores.  Outputs that no later step of the same kernel reads are
+// written non-temporally: plain stores leave dirty lines in the memory-side
+// cache, and the next kernel's reads then share the bandwidth with their
+// write-back (a 406 MB read after a 1 GB write took 2.3x as long).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
+
+// ---------------------------------------------------------------------------
 // BF16 <-> binary32
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

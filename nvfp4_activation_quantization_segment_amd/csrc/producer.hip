@@ -91,8 +91,8 @@ __device__ __forceinline__ void pack_block16_store(const uint32_t y[8], float s_
     uint2 w;
     w.x = quantize8(y, bq.d, bq.r, bq.fast) & bq.keep;
     w.y = quantize8(y + 4, bq.d, bq.r, bq.fast) & bq.keep;
-    *reinterpret_cast<uint2*>(qrow + 8 * b) = w;
-    srow[b] = (uint8_t)bq.sf;
+    store_nt(reinterpret_cast<uint2*>(qrow + 8 * b), w);
+    store_nt(srow + b, (uint8_t)bq.sf);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,8 +205,8 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
         if (rho >= g.R) break;
         // padding rows M .. rows_total-1 are zero
         for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
-            *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
-            sfa[r * sld + b] = 0;
+            store_nt(reinterpret_cast<uint2*>(qdata + r * qld + 8 * b), make_uint2(0u, 0u));
+            store_nt(sfa + r * sld + b, (uint8_t)0);
         }
         int64_t i = (int64_t)blockIdx.x * g.R + rho;
         if (i >= g.M) continue;
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
         const int b = idx - rho * C16;
         if (rho >= g.R) break;
         for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
-            *reinterpret_cast<uint2*>(qdata + r * qld + 8 * b) = make_uint2(0u, 0u);
-            sfa[r * sld + b] = 0;
+            store_nt(reinterpret_cast<uint2*>(qdata + r * qld + 8 * b), make_uint2(0u, 0u));
+            store_nt(sfa + r * sld + b, (uint8_t)0);
         }
         for (int64_t i = (int64_t)blockIdx.x * g.R + rho; i < g.M; i += GR) {
             const int64_t r = reverse ? g.M - 1 - i : i;
@@ -598,8 +598,8 @@ __device__ __forceinline__ void zero_pad_rows(const RowGeo& g, uint8_t* qdata, u
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = g.M + i / C16;
         const int b = (int)(i % C16);
-        *reinterpret_cast<uint2*>(qdata + r * 8 * C16 + 8 * b) = make_uint2(0u, 0u);
-        sfa[r * C16 + b] = 0;
+        store_nt(reinterpret_cast<uint2*>(qdata + r * 8 * C16 + 8 * b), make_uint2(0u, 0u));
+        store_nt(sfa + r * C16 + b, (uint8_t)0);
     }
 }
 

@@ -137,7 +137,8 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
  * so long that its wait passes 1 s, the call completes with a NaN tensor
  * scale and amax, scale code 0x7F and zero codes in every block, and so does
  * every later single-launch call on that workspace until it is zero-filled
- * again.  When D > 16384 it enqueues the two passes instead.  Same
+ * again.  When D > 16384, or x spans 4 GiB or more, it enqueues the two
+ * passes instead.  Same
  * requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack together. */
 nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                                      const nvfp4_segments* seg, void* workspace, float* tensor_scale,

@@ -145,8 +145,10 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
-    // one cooperative launch when a row fits one workgroup (D <= 16384)
-    const int G = D / 16 <= 1024 ? modulate_quantize_grid() : 0;
+    // one launch when a row fits one workgroup (D <= 16384) and every byte
+    // offset into x, qdata and sfa fits 32 bits
+    const bool off32 = ((M - 1) * ldx + D) * 2 < ((int64_t)1 << 32) && M_pad * (D / 2) < ((int64_t)1 << 32);
+    const int G = (D / 16 <= 1024 && off32) ? modulate_quantize_grid() : 0;
     if (G > 0) {
         const RowGeo g = row_geo(M, M_pad, D, ldx, G, 1, 16);
         return hip_status(launch_modulate_quantize(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, qdata,

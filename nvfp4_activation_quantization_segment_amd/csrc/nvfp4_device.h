@@ -23,16 +23,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Streaming stores.  Outputs that no later step of the same kernel reads are
-// written non-temporally: plain stores leave dirty lines in the memory-side
-// cache, and the next kernel's reads then share the bandwidth with their
-// write-back (a 406 MB read after a 1 GB write took 2.3x as long).
+// written non-temporally where a wave's store covers whole cache lines: plain
+// stores leave dirty lines in the memory-side cache, and the next kernel's
+// reads then share the bandwidth with their write-back (a 406 MB read after a
+// 1 GB write took 2.3x as long).  Stores that cover only parts of lines (the
+// bytes of a scale row) stay plain, so that the L2 merges them first.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 w = {v.x, v.y};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
 }
-__device__ __forceinline__ void store_nt(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
 
 // ---------------------------------------------------------------------------
 // BF16 <-> binary32
@@ -47,6 +48,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2 r = __builtin_convertvector(v, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
 }
+
+// RN(a) to bf16, returned as the binary32 value it equals: v_cvt_pk_bf16_f32
+// with a zero low half puts bf16(a) in the high half, which is that binary32
+// bit pattern (one instruction instead of a convert and an unpack).
+__device__ __forceinline__ float round_bf16(float a) { return __uint_as_float(pack_bf16x2(0.0f, a)); }
 
 // ---------------------------------------------------------------------------
 // Modulation: y = bf16(bf16(x * s1) + shift) with s1 = bf16(scale + 1)
@@ -182,13 +188,7 @@ __device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b) {
 // element 2j in the low nibble of byte j.  d = RN(sf*s_g), r = RN(1/d).
 // `fast` selects the Markstein quotient; otherwise correctly rounded division
 // with a NaN quotient mapped to code 0.
-__device__ __forceinline__ uint32_t quantize8(const uint32_t y[4], float d, float r, bool fast) {
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_lo(y[j]);
-        v[2 * j + 1] = bf16_hi(y[j]);
-    }
+__device__ __forceinline__ uint32_t quantize8f(const float v[8], float d, float r, bool fast) {
     float q[8];
     if (fast) {
 #pragma unroll
@@ -206,6 +206,16 @@ __device__ __forceinline__ uint32_t quantize8(const uint32_t y[4], float d, floa
     w = fp4_pack2<2>(w, q[4], q[5]);
     w = fp4_pack2<3>(w, q[6], q[7]);
     return w;
+}
+
+__device__ __forceinline__ uint32_t quantize8(const uint32_t y[4], float d, float r, bool fast) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_lo(y[j]);
+        v[2 * j + 1] = bf16_hi(y[j]);
+    }
+    return quantize8f(v, d, r, fast);
 }
 
 // Everything one block needs after its maximum is known.

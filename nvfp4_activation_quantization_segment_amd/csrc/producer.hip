@@ -92,7 +92,7 @@ __device__ __forceinline__ void pack_block16_store(const uint32_t y[8], float s_
     w.x = quantize8(y, bq.d, bq.r, bq.fast) & bq.keep;
     w.y = quantize8(y + 4, bq.d, bq.r, bq.fast) & bq.keep;
     store_nt(reinterpret_cast<uint2*>(qrow + 8 * b), w);
-    store_nt(srow + b, (uint8_t)bq.sf);
+    srow[b] = (uint8_t)bq.sf;
 }
 
 // ---------------------------------------------------------------------------
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
         // padding rows M .. rows_total-1 are zero
         for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
             store_nt(reinterpret_cast<uint2*>(qdata + r * qld + 8 * b), make_uint2(0u, 0u));
-            store_nt(sfa + r * sld + b, (uint8_t)0);
+            sfa[r * sld + b] = 0;
         }
         int64_t i = (int64_t)blockIdx.x * g.R + rho;
         if (i >= g.M) continue;
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(1024) void swiglu_pack_kernel(const uint16_t* __res
         if (rho >= g.R) break;
         for (int64_t r = g.M + (int64_t)blockIdx.x * g.R + rho; r < g.rows_total; r += GR) {
             store_nt(reinterpret_cast<uint2*>(qdata + r * qld + 8 * b), make_uint2(0u, 0u));
-            store_nt(sfa + r * sld + b, (uint8_t)0);
+            sfa[r * sld + b] = 0;
         }
         for (int64_t i = (int64_t)blockIdx.x * g.R + rho; i < g.M; i += GR) {
             const int64_t r = reverse ? g.M - 1 - i : i;
@@ -399,8 +399,9 @@ __device__ __forceinline__ void load_cols_pk(const SegParams& seg, int s, int b,
 __device__ __forceinline__ void modulate16_pk(const uint32_t xw[8], const ColPk& cp, uint32_t y[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint32_t p = pack_bf16x2(bf16_lo(xw[j]) * bf16_lo(cp.s1[j]), bf16_hi(xw[j]) * bf16_hi(cp.s1[j]));
-        y[j] = pack_bf16x2(bf16_lo(p) + bf16_lo(cp.sh[j]), bf16_hi(p) + bf16_hi(cp.sh[j]));
+        const float pa = round_bf16(bf16_lo(xw[j]) * bf16_lo(cp.s1[j]));
+        const float pb = round_bf16(bf16_hi(xw[j]) * bf16_hi(cp.s1[j]));
+        y[j] = pack_bf16x2(pa + bf16_lo(cp.sh[j]), pb + bf16_hi(cp.sh[j]));
     }
 }
 
@@ -599,77 +600,134 @@ __device__ __forceinline__ void zero_pad_rows(const RowGeo& g, uint8_t* qdata, u
         const int64_t r = g.M + i / C16;
         const int b = (int)(i % C16);
         store_nt(reinterpret_cast<uint2*>(qdata + r * 8 * C16 + 8 * b), make_uint2(0u, 0u));
-        store_nt(sfa + r * C16 + b, (uint8_t)0);
+        sfa[r * C16 + b] = 0;
     }
 }
 
+// Modulation of two packed columns with the product rounded by round_bf16
+// (one instruction fewer per pair than modulate2; same values).
+__device__ __forceinline__ uint32_t modulate2r(uint32_t x2, float s1a, float s1b, float sha, float shb) {
+    const float pa = round_bf16(bf16_lo(x2) * s1a), pb = round_bf16(bf16_hi(x2) * s1b);
+    return pack_bf16x2(pa + sha, pb + shb);
+}
+
+__device__ __forceinline__ void mod16_packed(const uint4& a, const uint4& c, const ColParams& p0, const ColParams& p1,
+                                             uint32_t y[8]) {
+    const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        y[j] = modulate2r(xw[j], p0.s1[2 * j], p0.s1[2 * j + 1], p0.sh[2 * j], p0.sh[2 * j + 1]);
+        y[4 + j] = modulate2r(xw[4 + j], p1.s1[2 * j], p1.s1[2 * j + 1], p1.sh[2 * j], p1.sh[2 * j + 1]);
+    }
+}
+
+// y of 16 columns as binary32 values (each exactly a bf16) and the largest
+// magnitude of the unrounded sums.  Rounding to bf16 is monotone and odd, so
+// the bf16 rounding of that maximum is the block's max |y|.  The maximum is a
+// binary32 max, which passes over NaN: used only in pass 2, where a finite
+// tensor scale means no y is NaN (a NaN y makes the global maximum NaN), and a
+// NaN tensor scale gives every block the NaN scale code whatever its maximum.
+__device__ __forceinline__ float mod16_f32(const uint4& a, const uint4& c, const ColParams& p0,
+                                           const ColParams& p1, float y[16]) {
+    const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const ColParams& p = j < 4 ? p0 : p1;
+        const int k = 2 * (j & 3);
+        const float sa = round_bf16(bf16_lo(xw[j]) * p.s1[k]) + p.sh[k];
+        const float sb = round_bf16(bf16_hi(xw[j]) * p.s1[k + 1]) + p.sh[k + 1];
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(sa), __builtin_fabsf(sb)));
+        y[2 * j] = round_bf16(sa);
+        y[2 * j + 1] = round_bf16(sb);
+    }
+    return m;
+}
+
+// Scale and codes of one block given as binary32 values and the maximum from
+// mod16_f32; stores its 8 QDATA bytes and scale byte.
+__device__ __forceinline__ void pack16f_store(const float y[16], float m, float s_g, float rg, bool sg_fast,
+                                              const float2* dr, uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+    const uint32_t a16 = __float_as_uint(round_bf16(m)) >> 16;
+    const BlockQ bq = block_setup_tab(a16, s_g, rg, sg_fast, dr);
+    uint2 w;
+    w.x = quantize8f(y, bq.d, bq.r, bq.fast) & bq.keep;
+    w.y = quantize8f(y + 8, bq.d, bq.r, bq.fast) & bq.keep;
+    store_nt(reinterpret_cast<uint2*>(q), w);
+    *sf = (uint8_t)bq.sf;
+}
+
+// Byte offsets within x, qdata and sfa fit 32 bits (checked by the caller),
+// so every access is a uniform base pointer plus a 32-bit offset.
+__device__ __forceinline__ uint4 ld16o(const char* base, uint32_t off) {
+    return *reinterpret_cast<const uint4*>(base + off);
+}
+
 // Pass 2 of the single launch: register-held groups, then LDS-held ones,
-// then the streamed groups last to first, whose column parameters are loaded
-// afresh (nothing of pass 1 stays live across the held groups).  Every thread
-// of the workgroup runs the loops (`on` guards the memory accesses) so that
-// the streamed loop can end each iteration with a workgroup barrier: left to
-// themselves the waves of a workgroup drift apart by ~30 us over this loop
-// (the first waves win the memory queue), and the last ones then finish alone
-// with too few loads in flight.
-__device__ __forceinline__ void pass2_mod(const uint16_t* __restrict__ x, const RowGeo& g, const SegParams& seg,
+// then the streamed groups last to first.  Every thread of the workgroup runs
+// the loops (`on` guards the memory accesses) so that the streamed loop can
+// end each iteration with a workgroup barrier: left to themselves the waves
+// of a workgroup drift apart by ~30 us over this loop and the last ones then
+// finish alone with too few loads in flight.
+__device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const RowGeo& g, const SegParams& seg,
                                           const uint32_t (&hy)[kHoldRegs][8], const uint4* hold, const HoldSplit& hs,
-                                          const float2* dr, float s_g, float rg, bool sg_fast, bool on,
-                                          int64_t r_first, int64_t gstride, int b, uint8_t* __restrict__ qdata,
+                                          const float2* dr, float s_g, float rg, bool sg_fast, bool on, int r_first,
+                                          int gstride, int b, uint8_t* __restrict__ qdata,
                                           uint8_t* __restrict__ sfa) {
     const int C16 = g.C8 >> 1;
-    const int64_t qld = 8 * (int64_t)C16, sld = C16;
+    const uint32_t xrow = 2u * (uint32_t)g.ldx, qrow = 8u * (uint32_t)C16, srow = (uint32_t)C16;
+    const uint32_t xcol = 32u * (uint32_t)b, qcol = 8u * (uint32_t)b;
     const int t0 = hs.ns + hs.nl;
     if (on) {
 #pragma unroll
         for (int h = 0; h < kHoldRegs; ++h) {
-            const int64_t r = r_first + (t0 + h) * gstride;
+            const int r = r_first + (t0 + h) * gstride;
             if (h < hs.nr && r < g.M)
-                pack_block16_store(hy[h], s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+                pack_block16_store(hy[h], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
+                                   b);
         }
         for (int h = hs.nl - 1; h >= 0; --h) {
-            const int64_t r = r_first + (hs.ns + h) * gstride;
+            const int r = r_first + (hs.ns + h) * gstride;
             uint32_t y[8];
             hold_get(hold, h, y);
-            pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+            pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow, b);
         }
     }
     int t = hs.ns - 1;
     if (t < 0) return;  // uniform over the workgroup
     int s2 = 0;
-    ColParams c0, c1;  // binary32 parameters: the streamed loop is short of VALU, not of registers
-    int64_t seg_lo = 0;  // rows decrease in this loop
+    ColParams c0, c1;  // binary32 parameters: this loop is short of VALU, not of registers
+    int seg_lo = 0;    // rows decrease in this loop
     if (on) {
         s2 = seg_find(seg, r_first + t * gstride, 0);
         load_cols(seg, s2, 2 * b, c0);
         load_cols(seg, s2, 2 * b + 1, c1);
-        seg_lo = seg.row_start[s2];
+        seg_lo = (int)seg.row_start[s2];
     }
-    auto pack = [&](const uint4& v0, const uint4& v1, int64_t r) {
+    auto pack = [&](const uint4& v0, const uint4& v1, int r) {
         if (r < seg_lo) {
             s2 = seg_find(seg, r, s2);
-            seg_lo = seg.row_start[s2];
+            seg_lo = (int)seg.row_start[s2];
             load_cols(seg, s2, 2 * b, c0);
             load_cols(seg, s2, 2 * b + 1, c1);
         }
-        uint32_t y[8];
-        modulate8(v0, c0, y);
-        modulate8(v1, c1, y + 4);
-        pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
+        float y[16];
+        const float m = mod16_f32(v0, v1, c0, c1, y);
+        pack16f_store(y, m, s_g, rg, sg_fast, dr, qdata + ((uint32_t)r * qrow + qcol), sfa + ((uint32_t)r * srow + b));
     };
     for (; t >= 1; t -= 2) {
         if (on) {
-            const int64_t r0 = r_first + t * gstride, r1 = r0 - gstride;
-            const uint16_t* p0 = x + r0 * g.ldx + 16 * b;
-            const uint16_t* p1 = x + r1 * g.ldx + 16 * b;
-            const uint4 a0 = ld16(p0), a1 = ld16(p0 + 8), b0 = ld16(p1), b1 = ld16(p1 + 8);
+            const int r0 = r_first + t * gstride, r1 = r0 - gstride;
+            const uint32_t o0 = (uint32_t)r0 * xrow + xcol, o1 = (uint32_t)r1 * xrow + xcol;
+            const uint4 a0 = ld16o(xb, o0), a1 = ld16o(xb, o0 + 16), b0 = ld16o(xb, o1), b1 = ld16o(xb, o1 + 16);
             pack(a0, a1, r0);
             pack(b0, b1, r1);
         }
         __syncthreads();
     }
     if (t == 0 && on) {
-        const uint16_t* p0 = x + r_first * g.ldx + 16 * b;
-        pack(ld16(p0), ld16(p0 + 8), r_first);
+        const uint32_t o0 = (uint32_t)r_first * xrow + xcol;
+        pack(ld16o(xb, o0), ld16o(xb, o0 + 16), r_first);
     }
 }
 
@@ -679,66 +737,67 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                                                                  uint8_t* __restrict__ sfa, int hold_lds) {
     __shared__ uint4 hold[kModHoldLdsBytes / 16];
     __shared__ float2 dr[128];
+    const char* xb = reinterpret_cast<const char*>(x);
     const int C16 = g.C8 >> 1;
     const int rho = threadIdx.x / C16, b = threadIdx.x - rho * C16;
     const bool on = rho < g.R;
     const int64_t groups = (g.M + g.R - 1) / g.R;
     const HoldSplit hs = hold_split(groups, hold_lds);
-    const int64_t gstride = (int64_t)gridDim.x * g.R;
-    const int64_t r_first = (int64_t)blockIdx.x * g.R + rho;  // row of local group 0
+    const int gstride = (int)gridDim.x * g.R;
+    const int r_first = (int)blockIdx.x * g.R + rho;  // row of local group 0
+    const uint32_t xrow = 2u * (uint32_t)g.ldx, xcol = 32u * (uint32_t)b;
     const uint64_t gen = grid_generation(ws);
 
     // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
     uint32_t m2 = 0;
     uint32_t hy[kHoldRegs][8];
-    // held groups: packed column parameters, loaded at their first row
-    int s = 0;
-    ColPk cp;
-    int64_t seg_hi = 0;  // rows increase in pass 1
-    // Streamed groups, two per iteration, with binary32 column parameters
-    // (short of VALU here, not of registers: the held groups come later).
     int t = 0;
     {
+        // streamed groups, two per iteration, with binary32 column parameters
+        // (short of VALU here, not of registers: the held groups come later)
         ColParams c0, c1;
-        int64_t hi = 0;
-        int sc = 0;
+        int hi = 0, sc = 0;
         if (on) {
             sc = seg_find(seg, r_first < g.M ? r_first : 0, 0);
             load_cols(seg, sc, 2 * b, c0);
             load_cols(seg, sc, 2 * b + 1, c1);
-            hi = seg.row_start[sc + 1];
+            hi = (int)seg.row_start[sc + 1];
         }
-        auto absmax = [&](const uint4& v0, const uint4& v1, int64_t r) {
+        auto absmax = [&](const uint4& v0, const uint4& v1, int r) {
             if (r >= hi) {
                 sc = seg_find(seg, r, sc);
-                hi = seg.row_start[sc + 1];
+                hi = (int)seg.row_start[sc + 1];
                 load_cols(seg, sc, 2 * b, c0);
                 load_cols(seg, sc, 2 * b + 1, c1);
             }
             uint32_t y[8];
-            modulate8(v0, c0, y);
-            modulate8(v1, c1, y + 4);
+            mod16_packed(v0, v1, c0, c1, y);
             max16(m2, y);
         };
         for (; t + 1 < hs.ns; t += 2) {
             if (on) {
-                const int64_t r0 = r_first + t * gstride, r1 = r0 + gstride;
-                const uint16_t* p0 = x + r0 * g.ldx + 16 * b;
-                const uint16_t* p1 = x + r1 * g.ldx + 16 * b;
-                const uint4 a0 = ld16(p0), a1 = ld16(p0 + 8), b0 = ld16(p1), b1 = ld16(p1 + 8);
+                const int r0 = r_first + t * gstride, r1 = r0 + gstride;
+                const uint32_t o0 = (uint32_t)r0 * xrow + xcol, o1 = (uint32_t)r1 * xrow + xcol;
+                const uint4 a0 = ld16o(xb, o0), a1 = ld16o(xb, o0 + 16), b0 = ld16o(xb, o1),
+                            b1 = ld16o(xb, o1 + 16);
                 absmax(a0, a1, r0);
                 absmax(b0, b1, r1);
             }
         }
     }
     if (on) {
+        // held groups: packed column parameters, loaded at their first row
+        int s = 0, seg_hi = 0;
+        ColPk cp;
         for (; t < hs.ns + hs.nl; ++t) {
-            const int64_t r = r_first + t * gstride;
-            uint32_t v[8], y[8];
-            ld32(x + r * g.ldx + 16 * b, v);
+            const int r = r_first + t * gstride;
+            const uint32_t o = (uint32_t)r * xrow + xcol;
+            const uint4 a = ld16o(xb, o), c = ld16o(xb, o + 16);
+            const uint32_t v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            uint32_t y[8];
             if (r >= seg_hi) {
                 s = seg_find(seg, r, s);
-                seg_hi = seg.row_start[s + 1];
+                seg_hi = (int)seg.row_start[s + 1];
                 load_cols_pk(seg, s, b, cp);
             }
             modulate16_pk(v, cp, y);
@@ -749,9 +808,12 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         const int t0 = hs.ns + hs.nl;
 #pragma unroll
         for (int h = 0; h < kHoldRegs; ++h) {
-            const int64_t r = r_first + (t0 + h) * gstride;
+            const int r = r_first + (t0 + h) * gstride;
             if (h < hs.nr && r < g.M) {
-                ld32(x + r * g.ldx + 16 * b, hy[h]);
+                const uint32_t o = (uint32_t)r * xrow + xcol;
+                const uint4 a = ld16o(xb, o), c = ld16o(xb, o + 16);
+                hy[h][0] = a.x; hy[h][1] = a.y; hy[h][2] = a.z; hy[h][3] = a.w;
+                hy[h][4] = c.x; hy[h][5] = c.y; hy[h][6] = c.z; hy[h][7] = c.w;
             } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) hy[h][k] = 0u;
@@ -759,11 +821,11 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         }
 #pragma unroll
         for (int h = 0; h < kHoldRegs; ++h) {
-            const int64_t r = r_first + (t0 + h) * gstride;
+            const int r = r_first + (t0 + h) * gstride;
             const bool valid = h < hs.nr && r < g.M;
             if (valid && r >= seg_hi) {
                 s = seg_find(seg, r, s);
-                seg_hi = seg.row_start[s + 1];
+                seg_hi = (int)seg.row_start[s + 1];
                 load_cols_pk(seg, s, b, cp);
             }
             uint32_t y[8];
@@ -782,7 +844,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
     zero_pad_rows(g, qdata, sfa);
-    pass2_mod(x, g, seg, hy, hold, hs, dr, s_g, rg, sg_fast, on, r_first, gstride, b, qdata, sfa);
+    pass2_mod(xb, g, seg, hy, hold, hs, dr, s_g, rg, sg_fast, on, r_first, gstride, b, qdata, sfa);
 }
 
 // ---------------------------------------------------------------------------

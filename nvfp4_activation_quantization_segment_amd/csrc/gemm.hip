@@ -362,6 +362,42 @@ gemm_kernel(GemmArgs a, GemmPart p) {
 
     // Epilogue: alpha = RN(s_a * s_w) applied in fp32, then bf16 (nearest-even).
     const float alpha = a.a_scale[0] * a.w_scale[0];
+    if ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0 && (a.ldo & 7) == 0) {
+        // Each wave stages its 128 x 64 bf16 sub-tile in LDS (rows of 144
+        // bytes) and writes it back as whole 128-byte rows, eight lanes per
+        // row, with non-temporal stores: the output (up to 1.6 GB) then leaves
+        // no dirty lines in the memory-side cache, which would slow the
+        // kernel that runs next (the following producer pass reads 0.4-2 GB).
+        constexpr int kRowB = 144;
+        char* wl = reinterpret_cast<char*>(lds) + wave * (kWM * kRowB);
+        __syncthreads();  // the last step's fragment reads are done
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16& c = acc[i][k];
+                    uint2 v;
+                    v.x = pack_bf16x2(c[4 * q + 0] * alpha, c[4 * q + 1] * alpha);
+                    v.y = pack_bf16x2(c[4 * q + 2] * alpha, c[4 * q + 3] * alpha);
+                    *reinterpret_cast<uint2*>(wl + (k * 32 + l32) * kRowB + (i * 32 + 8 * q + 4 * h) * 2) = v;
+                }
+        __syncthreads();
+        const int n = tn * kBN + wn * kWN + (lane & 7) * 8;
+        const int m0 = tm * kBM + wm * kWM + (lane >> 3);
+        if (n < a.N) {
+#pragma unroll
+            for (int it = 0; it < kWM / 8; ++it) {
+                const int m = m0 + 8 * it;
+                if (m < a.M) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
+                    store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int m = tm * kBM + wm * kWM + k * 32 + l32;

@@ -34,6 +34,11 @@ __device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
     const u32x2 w = {v.x, v.y};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
 }
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // BF16 <-> binary32

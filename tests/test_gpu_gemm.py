@@ -82,17 +82,39 @@ def test_ragged_shapes(m, M, N, K):
     check(ref, out_f64(out), f"{M}x{N}x{K}")
 
 
-def test_output_stride_and_untouched_padding(m):
-    """ldo > N: the columns beyond N are not written."""
+@pytest.mark.parametrize("extra", [8, 4])
+def test_output_stride_and_untouched_padding(m, extra):
+    """ldo > N: the columns beyond N are not written.  ldo = N + 8 takes the
+    epilogue that writes whole 16-byte chunks; ldo = N + 4 (rows only 8-byte
+    aligned) the one that writes 8 bytes per lane."""
     rng = np.random.default_rng(5)
     M, N, K = 70, 64, 128
     a = bf16_np(rng.standard_normal((M, K)))
     w = bf16_np(0.02 * rng.standard_normal((N, K)))
     sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, 128)
-    out = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M, ldo=N + 8)
+    out = gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M, ldo=N + extra)
     got = out_f64(out)
     assert np.isnan(got[:, N:]).all()
     check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), got[:, :N])
+
+
+def test_output_base_8_byte_aligned(m):
+    """An output base that is 8- but not 16-byte aligned takes the 8-byte
+    epilogue; the results match, and nothing before the base is written."""
+    rng = np.random.default_rng(15)
+    M, N, K = 300, 272, 128
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    dev = device()
+    buf = torch.full((M * N + 8,), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = buf[4:4 + M * N].view(M, N)
+    assert out.data_ptr() % 16 == 8
+    m.nvfp4_gemm(to_dev(qa), to_dev(sfa), to_dev(np.array([sa], np.float32)), M, qa.shape[0], to_dev(qw),
+                 to_dev(sfw), to_dev(np.array([sw], np.float32)), N, K, out, N)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:4]).all() and torch.isnan(buf[4 + M * N:]).all()
+    check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), out_f64(out))
 
 
 def test_identity_weight_returns_dequantized_activation(m):

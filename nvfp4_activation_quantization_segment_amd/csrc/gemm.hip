@@ -355,7 +355,11 @@ gemm_kernel(GemmArgs a, GemmPart p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x16& c = acc[i][k];
-                    dst[((i * 4 + k) * 4 + q) * 64] = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+                    // non-temporal: the next producer pass otherwise waits on these
+                    // lines' write-back from the memory-side cache
+                    store_nt(reinterpret_cast<uint4*>(&dst[((i * 4 + k) * 4 + q) * 64]),
+                             make_uint4(__float_as_uint(c[4 * q]), __float_as_uint(c[4 * q + 1]),
+                                        __float_as_uint(c[4 * q + 2]), __float_as_uint(c[4 * q + 3])));
                 }
         return;
     }

@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--summarize-trace", metavar="DIR", help="print the kernel table of a rocprofv3 trace run")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarize FETCH_SIZE/WRITE_SIZE runs and write profiles/traffic.json")
+    p.add_argument("--summarize-counters", metavar="DIR",
+                   help="per-kernel means of the counters of a rocprofv3 --pmc run of this script, and VALU lane-ops "
+                        "per element for the producer kernels (SQ_INSTS_VALU x 64 / elements)")
     p.add_argument("--summarize-mfma", metavar="DIR",
                    help="MFMA busy and clock per GEMM launch from a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
                         "SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE run")
@@ -91,6 +94,9 @@ def main():
         return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -544,6 +550,38 @@ def summarize_traffic(fetch_dir, write_dir):
         out.append(f"| {n.replace('nvfp4::', '')} | grid {g} | {fm / 1e6:.1f} | {wm / 1e6:.1f} | |")
     out.append("")
     out.append(f"profiles/traffic.json: gemm_kernel bytes_per_launch {int(bpl)} (source hash {entry['source_hash']})")
+    return "\n".join(out)
+
+
+def summarize_counters(d):
+    """Mean of each counter per kernel (dispatches grouped by kernel name and
+    grid), with the elements one launch covers for the producer kernels of the
+    step: modulation [37810, 5376], SwiGLU output [37810, 14336]."""
+    import numpy as np
+
+    rows = _csv_rows(d, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        k = int(r["Dispatch_Id"])
+        e = by.setdefault(k, {"name": _short(r["Kernel_Name"]), "grid": int(r["Grid_Size"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    groups = {}
+    for e in by.values():
+        if "nvfp4::" in e["name"]:
+            groups.setdefault((e["name"].replace("nvfp4::", ""), e["grid"]), []).append(e)
+    names = sorted({c for e in by.values() for c in e if c not in ("name", "grid")})
+    elems = {"modulate": 37810 * 5376, "swiglu": 37810 * 14336}
+    out = ["| kernel | grid | dispatches | " + " | ".join(names) + " | VALU lane-ops / element |",
+           "|---|---|---|" + "---|" * len(names) + "---|"]
+    for (n, g), es in sorted(groups.items(), key=lambda t: -len(t[1])):
+        means = [float(np.mean([e.get(c, 0.0) for e in es])) for c in names]
+        # the step's producer launches: 256 workgroups of 1024 (modulation) or 896 (SwiGLU) threads
+        kind = ("modulate" if "modulate" in n and g == 256 * 1024 else
+                "swiglu" if "swiglu" in n and "fill" not in n and g == 256 * 896 else None)
+        per = ""
+        if kind and "SQ_INSTS_VALU" in names:
+            per = f"{means[names.index('SQ_INSTS_VALU')] * 64 / elems[kind]:.2f}"
+        out.append(f"| {n} | {g} | {len(es)} | " + " | ".join(f"{m:.4g}" for m in means) + f" | {per} |")
     return "\n".join(out)
 
 

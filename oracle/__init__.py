@@ -65,6 +65,9 @@ _SIGS = {
     "ora_bf16_amax": (_F, [_P, _I64, _I64, _I64]),
     "ora_bf16_pack_rows": (None, [_P, _I64, _I64, _I64, _F, _I64, _I64, _P, _P]),
     "ora_gemm_rows": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _P, _I64, _P]),
+    "ora_gemm_bf16_rows": (None, [_P, _P, _F, _P, _P, _F, _I64, _I64, _P, _I64, _P]),
+    "ora_gate_residual": (_U16, [_U16, _U16, _U16]),
+    "ora_gate_residual_rows": (None, [_P, _I64, _I64, _I64, _I32, _P, _P, _I64, _P, _I64, _P, _I64]),
     "ora_modulate_amax_rows": (_F, [_P, _I64, _I64, _I32, _P, _P, _P, _I64, _I64, _I64]),
     "ora_swiglu_amax_rows": (_F, [_P, _P, _I64, _I64, _I64, _I64]),
     "ora_modulate_batch": (None, [_P, _P, _P, _I64, _P]),
@@ -290,6 +293,44 @@ def gemm_rows(qa, sfa, a_scale, qw, sfw, w_scale, rows) -> np.ndarray:
     out = np.empty((rows.size, N), np.float64)
     lib().ora_gemm_rows(_ptr(qa), _ptr(sfa), float(np.float32(a_scale)), _ptr(qw), _ptr(sfw),
                         float(np.float32(w_scale)), N, K, _ptr(rows), rows.size, _ptr(out))
+    return out
+
+
+def gemm_bf16_rows(qa, sfa, a_scale, qw, sfw, w_scale, rows) -> np.ndarray:
+    """BF16 outputs [len(rows), N] (uint16) with the sum rounded once to binary32:
+    the GEMM's bf16 output whenever its binary32 accumulation is exact."""
+    qa = _c(qa, np.uint8)
+    sfa = _c(sfa, np.uint8)
+    qw = _c(qw, np.uint8)
+    sfw = _c(sfw, np.uint8)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    N, Kh = qw.shape
+    K = Kh * 2
+    assert qa.shape[1] == Kh and sfa.shape[1] == K // 16 and sfw.shape == (N, K // 16)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < qa.shape[0])
+    out = np.empty((rows.size, N), np.uint16)
+    lib().ora_gemm_bf16_rows(_ptr(qa), _ptr(sfa), float(np.float32(a_scale)), _ptr(qw), _ptr(sfw),
+                             float(np.float32(w_scale)), N, K, _ptr(rows), rows.size, _ptr(out))
+    return out
+
+
+def gate_residual(o: int, gate: int, residual: int) -> int:
+    """bf16(residual + bf16(gate * o)) for one element."""
+    return int(lib().ora_gate_residual(int(o), int(gate), int(residual)))
+
+
+def gate_residual_rows(o, row_start, gate, residual) -> np.ndarray:
+    """The exact residual epilogue over o [M, N] (uint16 bf16 patterns): row m
+    uses gate row s of its segment [row_start[s], row_start[s+1])."""
+    o = _c(o, np.uint16)
+    gate = _c(gate, np.uint16)
+    residual = _c(residual, np.uint16)
+    rs = np.ascontiguousarray(np.asarray(row_start, dtype=np.int64))
+    M, N = o.shape
+    assert gate.shape[1] == N and residual.shape == (M, N) and rs[0] == 0 and rs[-1] == M
+    out = np.empty((M, N), np.uint16)
+    lib().ora_gate_residual_rows(_ptr(o), M, N, N, rs.size - 1, _ptr(rs), _ptr(gate), N, _ptr(residual), N,
+                                 _ptr(out), N)
     return out
 
 

@@ -340,6 +340,27 @@ void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Exact residual epilogue ("NVFP4 Streaming Design", P4: the BF16           */
+/* conversion, gate multiply, residual add and final BF16 rounding)          */
+/* ------------------------------------------------------------------------ */
+uint16_t ora_gate_residual(uint16_t o, uint16_t gate, uint16_t residual) {
+    float g = ora_bf16_to_f32(gate) * ora_bf16_to_f32(o);
+    float gb = ora_bf16_to_f32(ora_f32_to_bf16(g));
+    float r = ora_bf16_to_f32(residual) + gb;
+    return ora_f32_to_bf16(r);
+}
+
+void ora_gate_residual_rows(const uint16_t* o, int64_t M, int64_t N, int64_t ldo,
+                            int32_t nseg, const int64_t* row_start, const uint16_t* gate, int64_t ld_gate,
+                            const uint16_t* residual, int64_t ldr, uint16_t* out, int64_t ld_out) {
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* grow = gate + (int64_t)segment_of(m, nseg, row_start) * ld_gate;
+        for (int64_t n = 0; n < N; ++n)
+            out[m * ld_out + n] = ora_gate_residual(o[m * ldo + n], grow[n], residual[m * ldr + n]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM reference                                                            */
 /* ------------------------------------------------------------------------ */
 static double decoded(const uint8_t* q, const uint8_t* sf, int64_t row, int64_t k, int64_t K) {
@@ -368,4 +389,18 @@ void ora_gemm_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
     }
     free(wrow);
     free(arow);
+}
+
+void ora_gemm_bf16_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
+                        const uint8_t* qw, const uint8_t* sfw, float w_scale,
+                        int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* out) {
+    float alpha = a_scale * w_scale;
+    for (int64_t i = 0; i < nrows; ++i)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += decoded(qa, sfa, rows[i], k, K) * decoded(qw, sfw, n, k, K);
+            float sf = (float)s;
+            float o = alpha * sf;
+            out[i * N + n] = ora_f32_to_bf16(o);
+        }
 }

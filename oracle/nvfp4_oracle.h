@@ -91,12 +91,31 @@ void ora_element_code_batch(const uint16_t* y, const uint8_t* sf, int64_t n, flo
 void ora_e2m1_encode_batch(const float* v, int64_t n, uint8_t* code);
 void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code);
 
+/* ---- exact residual epilogue ("NVFP4 Streaming Design", P4) -------------- *
+ * After the BF16 conversion of the GEMM output o: gate multiply, residual add
+ * and final BF16 rounding, each a binary32 operation rounded to bf16:
+ *   out = bf16(residual + bf16(gate * o))                                   */
+uint16_t ora_gate_residual(uint16_t o, uint16_t gate, uint16_t residual);
+/* The same over o [M, N] (row stride ldo): gate is [nseg, N] bf16 (row stride
+ * ld_gate), row m using the gate row of its segment; residual [M, N] (row
+ * stride ldr); writes out [M, N] (row stride ld_out).                       */
+void ora_gate_residual_rows(const uint16_t* o, int64_t M, int64_t N, int64_t ldo,
+                            int32_t nseg, const int64_t* row_start, const uint16_t* gate, int64_t ld_gate,
+                            const uint16_t* residual, int64_t ldr, uint16_t* out, int64_t ld_out);
+
 /* ---- GEMM reference ----------------------------------------------------- *
  * out[i][n] = (double)RN32(a_scale*w_scale) * sum_k A[rows[i]][k] * W[n][k]
  * with A = e2m1(qa)*e4m3(sfa), W = e2m1(qw)*e4m3(sfw), all in binary64.    */
 void ora_gemm_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
                    const uint8_t* qw, const uint8_t* sfw, float w_scale,
                    int64_t N, int64_t K, const int64_t* rows, int64_t nrows, double* out);
+/* The BF16 output bf16(RN32(RN32(a_scale*w_scale) * RN32(S))) with S the
+ * binary64 sum above rounded once to binary32: the GEMM's BF16 output
+ * whenever the binary32 accumulation of the sum is exact (for example when
+ * every output is a single product, as with an identity weight).            */
+void ora_gemm_bf16_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
+                        const uint8_t* qw, const uint8_t* sfw, float w_scale,
+                        int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* out);
 
 #ifdef __cplusplus
 }

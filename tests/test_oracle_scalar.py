@@ -407,3 +407,50 @@ def test_e2m1_times_e4m3_products_are_exact_in_bf16(ora):
             assert b.to(torch.float16).to(torch.float64).item() == p
             n += 1
     assert n == 1016
+
+
+# --------------------------------------------------------------------------
+# Exact residual epilogue: out = bf16(residual + bf16(gate * o))
+# --------------------------------------------------------------------------
+def _torch_gate_residual(o, g, r):
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
+    return (to(r) + to(g) * to(o)).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_gate_residual_matches_torch_bf16_ops(ora):
+    """torch evaluates residual + gate * o on bf16 tensors as two binary32
+    operations, each rounded to bf16: the oracle's step, bit for bit (NaN
+    results compared as NaN)."""
+    rng = np.random.default_rng(21)
+    n = 60000
+    L = ora.lib()
+    for spread in (False, True):
+        o, g, r = (_random_bf16(rng, n, spread) for _ in range(3))
+        want = _torch_gate_residual(o, g, r)
+        got = np.fromiter((L.ora_gate_residual(int(a), int(b), int(c)) for a, b, c in zip(o, g, r)), np.uint16, n)
+        wn = np.isnan(bf16_to_f32_np(want))
+        ok = (got == want) | (wn & np.isnan(bf16_to_f32_np(got)))
+        assert ok.all(), np.flatnonzero(~ok)[:5]
+
+
+def test_gate_residual_rounds_the_product_first(ora):
+    """One rounding of the whole residual + gate * o gives different bytes on
+    some inputs; the oracle keeps the bf16 rounding of the product."""
+    rng = np.random.default_rng(22)
+    n = 40000
+    o, g, r = (_random_bf16(rng, n, False) for _ in range(3))
+    of, gf, rf = (bf16_to_f32_np(a).astype(np.float64) for a in (o, g, r))
+    single = (torch.from_numpy(rf + gf * of).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    L = ora.lib()
+    got = np.fromiter((L.ora_gate_residual(int(a), int(b), int(c)) for a, b, c in zip(o, g, r)), np.uint16, n)
+    assert np.count_nonzero(got != single) > 0
+    assert np.array_equal(got, _torch_gate_residual(o, g, r))
+
+
+def test_unit_gate_zero_residual_is_identity(ora):
+    """gate = 1 and residual = -0 return o bit-exactly for every non-NaN bf16."""
+    L = ora.lib()
+    for h in range(65536):
+        if (h & 0x7FFF) > 0x7F80:
+            continue
+        assert L.ora_gate_residual(h, 0x3F80, 0x8000) == h, hex(h)

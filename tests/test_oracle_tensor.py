@@ -218,6 +218,44 @@ def test_gemm_identity_weight_returns_dequantized_activation(ora):
     np.testing.assert_allclose(got, A * float(sa), rtol=2 ** -22)
 
 
+def test_gemm_bf16_output_for_an_identity_weight(ora):
+    """With W = I each output is one product (plus K-1 exact zeros), exact in
+    binary32, so the BF16 output is bf16(RN32(alpha * (2688 * A + 0))) with A
+    the dequantized activation
+    (torch's float32 -> bf16 cast as the rounding), and it lies within the
+    half-ulp of the FP64 reference."""
+    rng = np.random.default_rng(14)
+    M, K = 20, 128
+    a = nb(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32) * 3).to(torch.bfloat16))
+    sa, qa, sfa, _ = ora.quantize_bf16(a)
+    sw, qw, sfw, _ = ora.quantize_bf16(nb(torch.eye(K, dtype=torch.bfloat16)))
+    got = ora.gemm_bf16_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    A, _ = dequant_np(qa, sfa, 1.0)
+    alpha = np.float32(np.float32(sa) * np.float32(sw))
+    # the sum over K adds +0 terms to the one product, so a -0 product sums to +0
+    want = nb(torch.from_numpy((alpha * (A * 2688.0 + 0.0).astype(np.float32)).astype(np.float32)).to(torch.bfloat16))
+    assert np.array_equal(got, want)
+    ref = ora.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    gotf = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(gotf - ref) <= 2.0 ** -8 * np.abs(ref) * (1 + 2 ** -20))
+
+
+def test_gate_residual_rows_selects_the_segment_gate(ora):
+    """Row m uses the gate row of its segment; a shifted boundary changes rows."""
+    rng = np.random.default_rng(15)
+    M, N = 30, 48
+    bf = lambda v: nb(torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16))  # noqa: E731
+    o, res = bf(rng.standard_normal((M, N))), bf(rng.standard_normal((M, N)))
+    gate = bf(rng.standard_normal((3, N)))
+    rs = np.array([0, 7, 19, 30], np.int64)
+    got = ora.gate_residual_rows(o, rs, gate, res)
+    seg = np.searchsorted(rs[1:], np.arange(M), side="right")
+    want = nb(tb(res) + tb(gate)[torch.from_numpy(seg)] * tb(o))
+    assert np.array_equal(got, want)
+    other = ora.gate_residual_rows(o, np.array([0, 8, 19, 30], np.int64), gate, res)
+    assert not np.array_equal(other[7], got[7]) and np.array_equal(other[8:], got[8:])
+
+
 def test_tolerance_rule_detects_a_dropped_block(ora):
     """The GEMM tolerance rejects an output that misses one 16-wide K block."""
     rng = np.random.default_rng(12)

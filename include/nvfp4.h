@@ -199,6 +199,34 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a
                            int64_t N, int64_t K, uint16_t* out, int64_t ldo, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Per-segment gates of the residual epilogue: segment s covers output rows
+ * [row_start[s], row_start[s+1]) (count+1 HOST entries, 0 .. M, strictly
+ * increasing, 1 <= count <= NVFP4_MAX_SEGMENTS) and uses the DEVICE bf16 gate
+ * row gate[s * ld .. s * ld + N). */
+typedef struct {
+    int32_t count;
+    const int64_t* row_start;
+    const uint16_t* gate;
+    int64_t ld;
+} nvfp4_row_gates;
+
+/* nvfp4_gemm_ws followed by the exact residual epilogue ("NVFP4 Streaming
+ * Design", P4: the BF16 conversion, gate multiply, residual add and final BF16
+ * rounding), fused into the GEMM's store:
+ *   o   = bf16(RN(alpha * sum_k A[m][k] * W[n][k]))   (the nvfp4_gemm output)
+ *   out = bf16(RN(residual[m][n] + bf16(RN(gate[s][n] * o))))
+ * with s the segment of row m; residual is bf16 [M, ldr].  out may be the
+ * residual itself (same pointer and stride: each element is read before it is
+ * written, by the same thread); otherwise the two must not overlap.  Same
+ * requirements and workspace as nvfp4_gemm_ws, plus: gate and residual 8-byte
+ * aligned, gates->ld and ldr >= N and multiples of 4; a bad gate table returns
+ * NVFP4_ERR_SEGMENTS. */
+nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
+                                      int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
+                                      int64_t N, int64_t K, const nvfp4_row_gates* gates, const uint16_t* residual,
+                                      int64_t ldr, uint16_t* out, int64_t ldo, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* ---- Single-step entry points ------------------------------------------
  * Elementwise versions of single producer steps, running the very device
  * functions the producer kernels use, so that each step can be checked over

@@ -40,12 +40,18 @@ class Segments(ctypes.Structure):
                 ("shift", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("ld", ctypes.c_int64)]
 
 
+class RowGates(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("row_start", ctypes.POINTER(ctypes.c_int64)),
+                ("gate", ctypes.c_void_p), ("ld", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run nvfp4_activation_quantization_segment_amd/build.py")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I32, V = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     SEG = ctypes.POINTER(Segments)
+    GATES = ctypes.POINTER(RowGates)
     sigs = {
         "nvfp4_padded_rows": (I64, [I64]),
         "nvfp4_absmax_workspace_bytes": (ctypes.c_size_t, []),
@@ -57,6 +63,8 @@ def _load():
         "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
         "nvfp4_gemm_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64]),
         "nvfp4_gemm_ws": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, P, ctypes.c_size_t, V]),
+        "nvfp4_gemm_gate_residual": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, GATES, P, I64, P, I64, P,
+                                            ctypes.c_size_t, V]),
         "nvfp4_step_modulate": (I32, [P, P, P, P, I64, V]),
         "nvfp4_step_swiglu": (I32, [P, P, P, I64, V]),
         "nvfp4_step_block_scale": (I32, [P, P, P, I64, V]),
@@ -184,6 +192,24 @@ def nvfp4_gemm_ws(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, 
     _check("nvfp4_gemm_ws",
            lib.nvfp4_gemm_ws(_ptr(qa), _ptr(sfa), _ptr(a_scale), M, M_pad, _ptr(qw), _ptr(sfw), _ptr(w_scale), N, K,
                              _ptr(out), ldo, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def make_row_gates(row_start, gate: torch.Tensor):
+    """Build the C gate table; returns (struct, keepalive)."""
+    rs = (ctypes.c_int64 * len(row_start))(*[int(r) for r in row_start])
+    _bits16(gate)
+    if gate.dim() != 2 or gate.stride(1) != 1:
+        raise ValueError("gate must be [S, N] with unit column stride")
+    g = RowGates(len(row_start) - 1, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), gate.data_ptr(), gate.stride(0))
+    return g, (rs, gate)
+
+
+def nvfp4_gemm_gate_residual(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, gates, residual, ldr, out, ldo,
+                             workspace, workspace_bytes, stream=None):
+    _check("nvfp4_gemm_gate_residual",
+           lib.nvfp4_gemm_gate_residual(_ptr(qa), _ptr(sfa), _ptr(a_scale), M, M_pad, _ptr(qw), _ptr(sfw),
+                                        _ptr(w_scale), N, K, ctypes.byref(gates), _ptr(residual), ldr, _ptr(out), ldo,
+                                        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def nvfp4_step_modulate(x, scale, shift, y, n, stream=None):

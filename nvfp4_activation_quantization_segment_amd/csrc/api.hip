@@ -211,6 +211,13 @@ static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float
     a->M_pad = (int32_t)M_pad;
     a->N = (int32_t)N;
     a->K = (int32_t)K;
+    a->epi = 0;
+    a->nseg = 0;
+    memset(a->row_start, 0, sizeof(a->row_start));
+    a->gate = nullptr;
+    a->ld_gate = 0;
+    a->residual = nullptr;
+    a->ldr = 0;
     return NVFP4_OK;
 }
 
@@ -241,6 +248,37 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a
         if (!workspace || workspace_bytes < need) return NVFP4_ERR_INVALID_ARGUMENT;
         if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGNMENT;
     }
+    return hip_status(launch_gemm(a, (float*)workspace, need > 0, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
+                                      int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
+                                      int64_t N, int64_t K, const nvfp4_row_gates* gates, const uint16_t* residual,
+                                      int64_t ldr, uint16_t* out, int64_t ldo, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    GemmArgs a;
+    nvfp4_status st = gemm_args(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, &a);
+    if (st != NVFP4_OK) return st;
+    if (!gates || !gates->row_start || !gates->gate || !residual) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (gates->count < 1 || gates->count > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_SEGMENTS;
+    if (gates->row_start[0] != 0 || gates->row_start[gates->count] != M) return NVFP4_ERR_SEGMENTS;
+    for (int s = 0; s < gates->count; ++s)
+        if (gates->row_start[s + 1] <= gates->row_start[s]) return NVFP4_ERR_SEGMENTS;
+    if (gates->ld < N || ldr < N) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (gates->ld % 4 != 0 || ldr % 4 != 0 || !aligned(gates->gate, 8) || !aligned(residual, 8))
+        return NVFP4_ERR_ALIGNMENT;
+    const size_t need = gemm_plan(M, N, K).workspace_bytes;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return NVFP4_ERR_INVALID_ARGUMENT;
+        if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGNMENT;
+    }
+    a.epi = 1;
+    a.nseg = gates->count;
+    for (int s = 0; s <= gates->count; ++s) a.row_start[s] = (int32_t)gates->row_start[s];
+    a.gate = gates->gate;
+    a.ld_gate = gates->ld;
+    a.residual = residual;
+    a.ldr = ldr;
     return hip_status(launch_gemm(a, (float*)workspace, need > 0, (hipStream_t)stream));
 }
 

@@ -205,6 +205,33 @@ __device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_
     tn = (logical % gsz) / gm;
 }
 
+// Residual epilogue ("NVFP4 Streaming Design", P4: the BF16 conversion, gate
+// multiply, residual add and final BF16 rounding): for two packed outputs o2,
+// gates g2 and residuals r2, bf16(r + bf16(g * o)); the product of two bf16
+// values is exact in binary32.
+__device__ __forceinline__ uint32_t gate_residual2(uint32_t o2, uint32_t g2, uint32_t r2) {
+    const float pa = round_bf16(bf16_lo(g2) * bf16_lo(o2)), pb = round_bf16(bf16_hi(g2) * bf16_hi(o2));
+    return pack_bf16x2(bf16_lo(r2) + pa, bf16_hi(r2) + pb);
+}
+
+// Gate row of output row m (segments are contiguous row ranges).
+__device__ __forceinline__ const uint16_t* gate_row(const GemmArgs& a, int m) {
+    int s = 0;
+    while (s + 1 < a.nseg && m >= a.row_start[s + 1]) ++s;
+    return a.gate + (int64_t)s * a.ld_gate;
+}
+
+// The 8-byte store of 4 outputs at (m, n), through the epilogue when enabled.
+__device__ __forceinline__ void store_out4(const GemmArgs& a, int m, int n, uint2 v) {
+    if (a.epi) {
+        const uint2 g = *reinterpret_cast<const uint2*>(gate_row(a, m) + n);
+        const uint2 r = *reinterpret_cast<const uint2*>(a.residual + (int64_t)m * a.ldr + n);
+        v.x = gate_residual2(v.x, g.x, r.x);
+        v.y = gate_residual2(v.y, g.y, r.y);
+    }
+    *reinterpret_cast<uint2*>(a.out + (int64_t)m * a.ldo + n) = v;
+}
+
 // One launch's share of the output tiles.  The main launch computes tiles
 // [0, tiles) over all of K; a split launch computes `tiles` tail tiles from
 // tile_base on, each as ksplit K ranges of ks steps, and stores fp32 partial
@@ -366,7 +393,11 @@ gemm_kernel(GemmArgs a, GemmPart p) {
 
     // Epilogue: alpha = RN(s_a * s_w) applied in fp32, then bf16 (nearest-even).
     const float alpha = a.a_scale[0] * a.w_scale[0];
-    if ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0 && (a.ldo & 7) == 0) {
+    const bool rows16 = ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0 && (a.ldo & 7) == 0) &&
+                        (!a.epi || (((reinterpret_cast<uintptr_t>(a.gate) | reinterpret_cast<uintptr_t>(a.residual)) &
+                                     15) == 0 &&
+                                    ((a.ld_gate | a.ldr) & 7) == 0));
+    if (rows16) {
         // Each wave stages its 128 x 64 bf16 sub-tile in LDS (rows of 144
         // bytes) and writes it back as whole 128-byte rows, eight lanes per
         // row, with non-temporal stores: the output (up to 1.6 GB) then leaves
@@ -395,7 +426,15 @@ gemm_kernel(GemmArgs a, GemmPart p) {
             for (int it = 0; it < kWM / 8; ++it) {
                 const int m = m0 + 8 * it;
                 if (m < a.M) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
+                    uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
+                    if (a.epi) {
+                        const uint4 g = *reinterpret_cast<const uint4*>(gate_row(a, m) + n);
+                        const uint4 r = *reinterpret_cast<const uint4*>(a.residual + (int64_t)m * a.ldr + n);
+                        v.x = gate_residual2(v.x, g.x, r.x);
+                        v.y = gate_residual2(v.y, g.y, r.y);
+                        v.z = gate_residual2(v.z, g.z, r.z);
+                        v.w = gate_residual2(v.w, g.w, r.w);
+                    }
                     store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
                 }
             }
@@ -406,7 +445,6 @@ gemm_kernel(GemmArgs a, GemmPart p) {
     for (int k = 0; k < 4; ++k) {
         const int m = tm * kBM + wm * kWM + k * 32 + l32;
         if (m >= a.M) continue;
-        uint16_t* orow = a.out + (int64_t)m * a.ldo;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -417,7 +455,7 @@ gemm_kernel(GemmArgs a, GemmPart p) {
                 uint2 v;
                 v.x = pack_bf16x2(c[4 * q + 0] * alpha, c[4 * q + 1] * alpha);
                 v.y = pack_bf16x2(c[4 * q + 2] * alpha, c[4 * q + 3] * alpha);
-                *reinterpret_cast<uint2*>(orow + n) = v;
+                store_out4(a, m, n, v);
             }
         }
     }
@@ -443,7 +481,6 @@ __global__ __launch_bounds__(64) void gemm_finalize_kernel(GemmArgs a, GemmPart 
     const size_t slot = (size_t)8 * 32 * 64;  // float4 per partial tile
     const float4* src = reinterpret_cast<const float4*>(p.partial) + (size_t)tail * p.ksplit * slot +
                         (size_t)wave * (32 * 64) + lane;
-    uint16_t* orow = a.out + (int64_t)m * a.ldo;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -467,7 +504,7 @@ __global__ __launch_bounds__(64) void gemm_finalize_kernel(GemmArgs a, GemmPart 
             uint2 w;
             w.x = pack_bf16x2(acc.x * alpha, acc.y * alpha);
             w.y = pack_bf16x2(acc.z * alpha, acc.w * alpha);
-            *reinterpret_cast<uint2*>(orow + n) = w;
+            store_out4(a, m, n, w);
         }
     }
 }

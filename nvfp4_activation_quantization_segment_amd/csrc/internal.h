@@ -65,6 +65,15 @@ struct GemmArgs {
     uint16_t* out;
     int64_t ldo;
     int32_t M, M_pad, N, K;
+    // Residual epilogue (epi != 0): out = bf16(residual + bf16(gate[s][n] * o)),
+    // s the segment of row m (row_start has nseg + 1 entries).
+    int32_t epi;
+    int32_t nseg;
+    int32_t row_start[NVFP4_MAX_SEGMENTS + 1];
+    const uint16_t* gate;
+    int64_t ld_gate;
+    const uint16_t* residual;
+    int64_t ldr;
 };
 // Tiles of one GEMM launch (see gemm.hip).
 struct GemmPart {

@@ -394,13 +394,14 @@ void ora_gemm_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
 void ora_gemm_bf16_rows(const uint8_t* qa, const uint8_t* sfa, float a_scale,
                         const uint8_t* qw, const uint8_t* sfw, float w_scale,
                         int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* out) {
+    /* the binary64 sums S (unit scales), then bf16(RN32(alpha * RN32(S))) */
+    double* sums = (double*)malloc(sizeof(double) * (size_t)(nrows * N));
+    ora_gemm_rows(qa, sfa, 1.0f, qw, sfw, 1.0f, N, K, rows, nrows, sums);
     float alpha = a_scale * w_scale;
-    for (int64_t i = 0; i < nrows; ++i)
-        for (int64_t n = 0; n < N; ++n) {
-            double s = 0.0;
-            for (int64_t k = 0; k < K; ++k) s += decoded(qa, sfa, rows[i], k, K) * decoded(qw, sfw, n, k, K);
-            float sf = (float)s;
-            float o = alpha * sf;
-            out[i * N + n] = ora_f32_to_bf16(o);
-        }
+    for (int64_t i = 0; i < nrows * N; ++i) {
+        float sf = (float)sums[i];
+        float o = alpha * sf;
+        out[i] = ora_f32_to_bf16(o);
+    }
+    free(sums);
 }

@@ -74,6 +74,13 @@ def gemm_rows(qa, sfa, a_scale, qw, sfw, w_scale, rows):
     return np.concatenate(outs, axis=0)
 
 
+def gemm_bf16_rows(qa, sfa, a_scale, qw, sfw, w_scale, rows):
+    rows = np.asarray(rows, np.int64)
+    chunks = [rows[a:b] for a, b in _ranges(rows.size, WORKERS)]
+    outs = _map(lambda r: oracle.gemm_bf16_rows(qa, sfa, a_scale, qw, sfw, w_scale, r), chunks)
+    return np.concatenate(outs, axis=0)
+
+
 def batch(fn, n, *arrays):
     """fn(*slices) -> array; applied to chunks of the flattened inputs."""
     arrays = [np.ascontiguousarray(a).ravel() for a in arrays]

@@ -124,6 +124,29 @@ def test_producer_argument_errors(pkg):
     assert L.nvfp4_swiglu_pack(FAKE, None, 10, 32, 64, ts, q, s, 64, None) == 1
 
 
+def test_gate_residual_argument_errors(pkg):
+    g = pkg.lib.nvfp4_gemm_gate_residual
+    P = FAKE
+    rs = (ctypes.c_int64 * 3)(0, 5, 10)
+    gates = pkg.RowGates(2, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), P, 64)
+    args = lambda **k: dict(dict(M=10, N=64, K=64, gates=ctypes.byref(gates), res=P, ldr=64, out=P, ldo=64), **k)  # noqa: E731
+    call = lambda a: g(P, P, P, a["M"], 64, P, P, P, a["N"], a["K"], a["gates"], a["res"], a["ldr"], a["out"],  # noqa: E731
+                       a["ldo"], P, 1 << 20, None)
+    assert call(args(res=None)) == 1                   # no residual
+    assert call(args(gates=None)) == 1                 # no gate table
+    assert call(args(K=48)) == 2                       # K % 64, as nvfp4_gemm
+    assert call(args(ldr=60)) == 1                     # ldr < N
+    assert call(args(ldr=66)) == 3                     # ldr % 4
+    assert call(args(res=P + 4)) == 3                  # residual alignment
+    bad = (ctypes.c_int64 * 3)(0, 5, 9)
+    gb = pkg.RowGates(2, ctypes.cast(bad, ctypes.POINTER(ctypes.c_int64)), P, 64)
+    assert call(args(gates=ctypes.byref(gb))) == 4     # last row != M
+    zero = pkg.RowGates(0, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), P, 64)
+    assert call(args(gates=ctypes.byref(zero))) == 4   # no segments
+    short = pkg.RowGates(2, ctypes.cast(rs, ctypes.POINTER(ctypes.c_int64)), P, 32)
+    assert call(args(gates=ctypes.byref(short))) == 1  # gate ld < N
+
+
 def test_status_strings(pkg):
     for st in range(6):
         assert pkg.lib.nvfp4_status_string(st)

@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 from tests import _par
-from tests.gpu_util import device, host, host_u16, to_dev, to_dev_u16
+from tests.gpu_util import device, first_mismatch, host, host_u16, to_dev, to_dev_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -306,3 +306,77 @@ def test_split_tail_with_4byte_aligned_scales(m):
                     offset_copy(sfw, 4), to_dev(np.array([sw], np.float32)), N, K, out, N, ws, need)
     torch.cuda.synchronize()
     check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M)), out_f64(out), "ws misaligned scales")
+
+
+# --------------------------------------------------------------------------
+# Exact residual epilogue: out = bf16(residual + bf16(gate[s][n] * o))
+# --------------------------------------------------------------------------
+def gpu_gate_residual(m, sa, qa, sfa, sw, qw, sfw, M, rs, gate, residual, ldo=None, in_place=False):
+    dev = device()
+    N, K = qw.shape[0], 2 * qw.shape[1]
+    ldo = N if ldo is None else ldo
+    res = torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device=dev)
+    res[:, :N] = to_dev_u16(residual)
+    out = res if in_place else torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device=dev)
+    gates, keep = m.make_row_gates(rs, to_dev_u16(gate))
+    need = m.nvfp4_gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    m.nvfp4_gemm_gate_residual(to_dev(qa), to_dev(sfa), to_dev(np.array([sa], np.float32)), M, qa.shape[0],
+                               to_dev(qw), to_dev(sfw), to_dev(np.array([sw], np.float32)), N, K, gates, res, ldo,
+                               out, ldo, ws, need)
+    torch.cuda.synchronize()
+    del keep
+    return host_u16(out)
+
+
+@pytest.mark.parametrize("M,K,segs,extra,in_place", [
+    (200, 256, (0, 37, 150, 200), 0, False),     # 16-byte staged stores
+    (200, 256, (0, 37, 150, 200), 0, True),      # out is the residual
+    (130, 192, (0, 1, 129, 130), 4, False),      # rows 8-byte aligned only: 8-byte stores
+    (64, 5376, (0, 20, 64), 0, False),           # one row of tiles: K-split pieces and the finalize kernel
+])
+def test_gate_residual_identity_weight_bit_exact(m, M, K, segs, extra, in_place):
+    """With W = I every output is one product, so the GEMM's bf16 output is
+    exact and the fused epilogue is compared with the oracle bit for bit."""
+    rng = np.random.default_rng(M + K)
+    a = bf16_np(3 * rng.standard_normal((M, K)))
+    sa, qa, sfa, _ = _par.quantize_bf16(a, oracle.padded_rows(M))
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    sw, qw, sfw, _ = _par.quantize_bf16(eye)
+    S = len(segs) - 1
+    gate = bf16_np(1 + 0.3 * rng.standard_normal((S, K)))
+    residual = bf16_np(rng.standard_normal((M, K)))
+    rs = np.array(segs, np.int64)
+    o = _par.gemm_bf16_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    want = oracle.gate_residual_rows(o, rs, gate, residual)
+    got = gpu_gate_residual(m, sa, qa, sfa, sw, qw, sfw, M, rs, gate, residual, ldo=K + extra, in_place=in_place)
+    assert np.array_equal(got[:, :K], want), first_mismatch(got[:, :K], want)
+    if extra:
+        assert np.isnan((got[:, K:].astype(np.uint32) << 16).view(np.float32)).all()
+
+
+def test_gate_residual_random_within_tolerance(m):
+    """Random operands: out against the FP64 reference residual + gate * ref,
+    within the GEMM tolerance carried through the gate product plus one bf16
+    half-ulp for each of the two further roundings."""
+    rng = np.random.default_rng(31)
+    M, N, K = 300, 272, 512
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    rs = np.array([0, 100, 300], np.int64)
+    gate = bf16_np(0.5 * rng.standard_normal((2, N)))
+    residual = bf16_np(rng.standard_normal((M, N)))
+    got = (gpu_gate_residual(m, sa, qa, sfa, sw, qw, sfw, M, rs, gate, residual).astype(np.uint32) << 16)
+    got = got.view(np.float32).astype(np.float64)
+    ref_o = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    seg = np.searchsorted(rs[1:], np.arange(M), side="right")
+    g = (gate.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[seg]
+    r = (residual.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = r + g * ref_o
+    e_o = 2.0 ** -7 * np.abs(ref_o) + 1e-3 * np.sqrt(np.mean(ref_o ** 2))
+    e_g = np.abs(g) * e_o + 2.0 ** -8 * np.abs(g) * (np.abs(ref_o) + e_o)
+    bound = e_g + 2.0 ** -8 * (np.abs(ref) + e_g) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float(np.max(err / bound))

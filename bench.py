@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-attn-out", action="store_true",
+                   help="skip the separately timed attention-output projection")
     p.add_argument("--two-pass", action="store_true",
                    help="run the modulation producers as two launches (absmax, pack) instead of the single launch")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
@@ -313,9 +315,64 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_attn_out:
+        result["attn_out"] = attn_out_projection(nv, synth, dev, stream, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, x_h, segs, gu_h, (wq, wf1, wf2))
     print(json.dumps(result), flush=True)
+
+
+def attn_out_projection(nv, synth, dev, stream, reps):
+    """The attention-output projection, timed on its own after the step (not
+    part of `value`): the plain quantizer on the attention values [37810, 7168]
+    and the GEMM to the model width 5376 with the residual epilogue
+    out = bf16(residual + bf16(gate * o)) written in place into the residual."""
+    import numpy as np
+    import torch
+
+    w = synth.workload("attn_out")
+    M, K, N, M_pad = w.M, w.K, w.N, w.m_pad
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = up(w.x())
+    wt = up(w.weight())
+    rs, gate = w.gates()
+    residual0 = up(w.residual())
+    residual = residual0.clone()
+    gates, keep = nv.make_row_gates(rs, up(gate))
+    with torch.cuda.stream(stream):
+        qw, sfw, tw = nv.quantize_weight(wt, stream=stream)
+    q = torch.empty((M_pad, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M_pad, K // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.zeros(int(nv.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
+    need = nv.nvfp4_gemm_workspace_bytes(M, N, K)
+    gws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 1)]
+    for k in range(reps + 1):  # the first is a warm-up
+        ev[k][0].record(stream)
+        nv.nvfp4_quantize(x, M, K, K, ws, ts, None, q, s, M_pad, stream)
+        ev[k][1].record(stream)
+        nv.nvfp4_gemm_gate_residual(q, s, ts, M, M_pad, qw, sfw, tw, N, K, gates, residual, N, residual, N, gws,
+                                    need, stream)
+        ev[k][2].record(stream)
+    stream.synchronize()
+    pq = float(np.median([e[0].elapsed_time(e[1]) for e in ev[1:]]))
+    pg = float(np.median([e[1].elapsed_time(e[2]) for e in ev[1:]]))
+    pbytes = 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
+    flop = 2.0 * M * N * K
+    del keep
+    return {
+        "workload": "plain quantizer on [37810, 7168] -> NVFP4 GEMM N=5376 with the residual epilogue (2 gate "
+                    "segments, residual updated in place); timed on its own, not part of value",
+        "producer_ms": round(pq, 4), "producer_GBps": round(pbytes / (pq * 1e-3) / 1e9, 1),
+        "producer_frac_hbm": round(pbytes / (pq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "gemm_ms": round(pg, 4), "gemm_TFLOPs": round(flop / (pg * 1e-3) / 1e12, 1),
+        "gemm_frac_peak": round(flop / (pg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+    }
 
 
 def _oracle_weight(oracle, wt):

@@ -145,6 +145,15 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
                                      float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
                                      void* stream);
 
+/* The plain quantizer: nvfp4_modulate_quantize with y = x (no modulation), for
+ * activations that need none (the attention-output projection's input,
+ * "NVFP4 Streaming Design", P0/P2: the widths 5376, 7168, 14336) and for
+ * prepacking weights.  Same launch structure, outputs, workspace and
+ * requirements, without the segment table. */
+nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx, void* workspace,
+                            float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
+                            void* stream);
+
 /* Pass 1 of the SwiGLU producer ("FC2 NVFP4 Library Scheduling", Exact
  * Operation and Current Baseline: exact BF16 SwiGLU fused into NVFP4
  * production).  h = bf16(bf16(silu(g)) * u) with silu(g) = g / (1 + exp(-g))

@@ -58,6 +58,7 @@ def _load():
         "nvfp4_modulate_absmax": (I32, [P, I64, I64, I64, SEG, P, P, P, V]),
         "nvfp4_modulate_pack": (I32, [P, I64, I64, I64, SEG, P, P, P, I64, V]),
         "nvfp4_modulate_quantize": (I32, [P, I64, I64, I64, SEG, P, P, P, P, P, I64, V]),
+        "nvfp4_quantize": (I32, [P, I64, I64, I64, P, P, P, P, P, I64, V]),
         "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
         "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
         "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
@@ -163,6 +164,12 @@ def nvfp4_modulate_quantize(x, M, D, ldx, seg, ws, tensor_scale, amax_out, qdata
     _check("nvfp4_modulate_quantize",
            lib.nvfp4_modulate_quantize(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(ws), _ptr(tensor_scale),
                                        _ptr(amax_out), _ptr(qdata), _ptr(sfa), M_pad, _stream(stream)))
+
+
+def nvfp4_quantize(x, M, D, ldx, ws, tensor_scale, amax_out, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_quantize",
+           lib.nvfp4_quantize(_ptr(x), M, D, ldx, _ptr(ws), _ptr(tensor_scale), _ptr(amax_out), _ptr(qdata), _ptr(sfa),
+                              M_pad, _stream(stream)))
 
 
 def nvfp4_swiglu_absmax(gate, up, M, F, ld, ws, tensor_scale, amax_out=None, stream=None):
@@ -286,13 +293,27 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None):
     return q, s, ts, amax
 
 
+def quantize(x: torch.Tensor, m_pad: int | None = None, stream=None):
+    """Plain quantizer: x [M, D] bf16 -> (qdata [M_pad, D/2], sfa [M_pad, D/16], tensor_scale f32[1], amax f32[1])."""
+    _bits16(x)
+    M, D = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    m_pad = padded_rows(M) if m_pad is None else m_pad
+    dev = x.device
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev), ts, amax, q, s, m_pad, stream)
+    return q, s, ts, amax
+
+
 def quantize_weight(w: torch.Tensor, stream=None):
-    """Prepack a bf16 weight [N, K] to NVFP4 with the identity modulation
-    (scale = +0, shift = -0): returns (qw [N, K/2], sfw [N, K/16], w_scale f32[1])."""
+    """Prepack a bf16 weight [N, K] to NVFP4 with the plain quantizer: returns
+    (qw [N, K/2], sfw [N, K/16], w_scale f32[1])."""
     N, K = w.shape
-    shift = torch.full((1, K), -0.0, dtype=torch.bfloat16, device=w.device)
-    scale = torch.zeros((1, K), dtype=torch.bfloat16, device=w.device)
-    q, s, ts, _ = modulate_quantize(w, [0, N], shift, scale, stream=stream)
+    q, s, ts, _ = quantize(w, stream=stream)
     return q[:N], s[:N], ts
 
 

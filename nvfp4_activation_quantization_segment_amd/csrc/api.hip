@@ -116,7 +116,7 @@ nvfp4_status nvfp4_modulate_absmax(const uint16_t* x, int64_t M, int64_t D, int6
     if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
     const RowGeo g = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
-    return hip_status(launch_modulate_absmax(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out,
+    return hip_status(launch_modulate_absmax(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, false,
                                              (hipStream_t)stream));
 }
 
@@ -131,7 +131,30 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
     if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     const RowGeo g = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
-    return hip_status(launch_modulate_pack(x, g, sp, tensor_scale, qdata, sfa, (hipStream_t)stream));
+    return hip_status(launch_modulate_pack(x, g, sp, tensor_scale, qdata, sfa, false, (hipStream_t)stream));
+}
+
+// Both passes, as one launch where it applies, else as the two passes; the
+// plain quantizer passes plain = true and a segment table that is never read.
+static nvfp4_status quantize_both(const uint16_t* x, int64_t M, int64_t D, int64_t ldx, const SegParams& sp,
+                                  bool plain, void* workspace, float* tensor_scale, float* amax_out,
+                                  uint8_t* qdata, uint8_t* sfa, int64_t M_pad, hipStream_t s) {
+    // one launch when a row fits one workgroup (D <= 16384) and every byte
+    // offset into x, qdata and sfa fits 32 bits
+    const bool off32 = ((M - 1) * ldx + D) * 2 < ((int64_t)1 << 32) && M_pad * (D / 2) < ((int64_t)1 << 32);
+    const int G = (D / 16 <= 1024 && off32) ? modulate_quantize_grid() : 0;
+    if (G > 0) {
+        const RowGeo g = row_geo(M, M_pad, D, ldx, G, 1, 16);
+        return hip_status(launch_modulate_quantize(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, qdata,
+                                                   sfa, plain, s));
+    }
+    nvfp4_status st;
+    const RowGeo g1 = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
+    if ((st = hip_status(launch_modulate_absmax(x, g1, sp, (uint32_t*)workspace, tensor_scale, amax_out, plain, s))) !=
+        NVFP4_OK)
+        return st;
+    const RowGeo g2 = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
+    return hip_status(launch_modulate_pack(x, g2, sp, tensor_scale, qdata, sfa, plain, s));
 }
 
 nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
@@ -144,22 +167,24 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
     if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
-    const hipStream_t s = (hipStream_t)stream;
-    // one launch when a row fits one workgroup (D <= 16384) and every byte
-    // offset into x, qdata and sfa fits 32 bits
-    const bool off32 = ((M - 1) * ldx + D) * 2 < ((int64_t)1 << 32) && M_pad * (D / 2) < ((int64_t)1 << 32);
-    const int G = (D / 16 <= 1024 && off32) ? modulate_quantize_grid() : 0;
-    if (G > 0) {
-        const RowGeo g = row_geo(M, M_pad, D, ldx, G, 1, 16);
-        return hip_status(launch_modulate_quantize(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, qdata,
-                                                   sfa, s));
-    }
-    const RowGeo g1 = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
-    if ((st = hip_status(launch_modulate_absmax(x, g1, sp, (uint32_t*)workspace, tensor_scale, amax_out, s))) !=
-        NVFP4_OK)
-        return st;
-    const RowGeo g2 = row_geo(M, M_pad, D, ldx, kPackWgs, 1, 16);
-    return hip_status(launch_modulate_pack(x, g2, sp, tensor_scale, qdata, sfa, s));
+    return quantize_both(x, M, D, ldx, sp, false, workspace, tensor_scale, amax_out, qdata, sfa, M_pad,
+                         (hipStream_t)stream);
+}
+
+nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx, void* workspace,
+                            float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
+                            void* stream) {
+    nvfp4_status st = check_rows(x, M, D, ldx);
+    if (st != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    SegParams sp;  // one segment over all rows; its parameters are never read
+    memset(&sp, 0, sizeof(sp));
+    sp.count = 1;
+    sp.row_start[1] = M;
+    return quantize_both(x, M, D, ldx, sp, true, workspace, tensor_scale, amax_out, qdata, sfa, M_pad,
+                         (hipStream_t)stream);
 }
 
 nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,

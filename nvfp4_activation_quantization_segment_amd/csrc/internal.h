@@ -36,9 +36,9 @@ struct RowGeo {
 enum StepKind { STEP_MODULATE, STEP_SWIGLU, STEP_BLOCK_SCALE, STEP_ELEMENT_CODE, STEP_E2M1, STEP_E4M3 };
 
 hipError_t launch_modulate_absmax(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
-                                  float* tensor_scale, float* amax_out, hipStream_t s);
+                                  float* tensor_scale, float* amax_out, bool plain, hipStream_t s);
 hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegParams& seg, const float* tensor_scale,
-                                uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+                                uint8_t* qdata, uint8_t* sfa, bool plain, hipStream_t s);
 // Single-pass producer: one launch of at most modulate_quantize_grid()
 // workgroups, all resident at once (0 when that cannot be determined).  The
 // workspace holds one 8-byte arrival word per workgroup after 256 header bytes.
@@ -46,8 +46,9 @@ constexpr int kMaxDevices = 32;
 constexpr int kMaxGridSlots = 1024;
 constexpr size_t kWorkspaceBytes = 256 + 8 * kMaxGridSlots;
 int modulate_quantize_grid();
+// plain: the plain quantizer (y = x; seg is not read).
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
-                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
                                     hipStream_t s);
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, hipStream_t s);

@@ -134,6 +134,8 @@ __device__ __forceinline__ int seg_advance(const SegParams& seg, int64_t r, int 
 // Rows are assigned grid-stride (workgroup b takes rows b, b+G, b+2G, ...), so
 // the workgroups resident at any moment read one compact window of the tensor
 // that sweeps through it, which is what the memory system streams best.
+// PLAIN: y = x (the plain quantizer; seg is not read).
+template <bool PLAIN>
 __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                                SegParams seg, uint32_t* ws,
                                                                float* tensor_scale, float* amax_out) {
@@ -146,32 +148,41 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
         int s = seg_advance(seg, r < g.M ? r : 0, 0);
         int64_t seg_end = seg.row_start[s + 1];  // rows only increase: one compare per row
         ColParams cp;
-        load_cols(seg, s, c, cp);
+        if (!PLAIN) load_cols(seg, s, c, cp);
         for (; r + 3 * G < g.M; r += 4 * G) {
             uint4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = ld16(x + (r + u * G) * g.ldx + 8 * c);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (r + u * G >= seg_end) {
-                    s = seg_advance(seg, r + u * G, s);
-                    seg_end = seg.row_start[s + 1];
-                    load_cols(seg, s, c, cp);
-                }
                 uint32_t y[4];
-                modulate8(v[u], cp, y);
+                if constexpr (PLAIN) {
+                    y[0] = v[u].x; y[1] = v[u].y; y[2] = v[u].z; y[3] = v[u].w;
+                } else {
+                    if (r + u * G >= seg_end) {
+                        s = seg_advance(seg, r + u * G, s);
+                        seg_end = seg.row_start[s + 1];
+                        load_cols(seg, s, c, cp);
+                    }
+                    modulate8(v[u], cp, y);
+                }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
             }
         }
         for (; r < g.M; r += G) {
-            if (r >= seg_end) {
-                s = seg_advance(seg, r, s);
-                seg_end = seg.row_start[s + 1];
-                load_cols(seg, s, c, cp);
-            }
             uint32_t y[4];
-            modulate8(ld16(x + r * g.ldx + 8 * c), cp, y);
+            const uint4 xv = ld16(x + r * g.ldx + 8 * c);
+            if constexpr (PLAIN) {
+                y[0] = xv.x; y[1] = xv.y; y[2] = xv.z; y[3] = xv.w;
+            } else {
+                if (r >= seg_end) {
+                    s = seg_advance(seg, r, s);
+                    seg_end = seg.row_start[s + 1];
+                    load_cols(seg, s, c, cp);
+                }
+                modulate8(xv, cp, y);
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
         }
@@ -183,6 +194,7 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
 // block scale is computed once.  Rows are walked last-to-first (grid-stride
 // from the end), so the rows pass 1 read last, which are still in the
 // memory-side cache, are read first.
+template <bool PLAIN>
 __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                              SegParams seg, const float* tensor_scale,
                                                              uint8_t* __restrict__ qdata,
@@ -215,23 +227,30 @@ __global__ __launch_bounds__(1024) void modulate_pack_kernel(const uint16_t* __r
         while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
         int64_t seg_lo = seg.row_start[s], seg_hi = seg.row_start[s + 1];
         ColParams cp0, cp1;
-        load_cols(seg, s, 2 * b, cp0);
-        load_cols(seg, s, 2 * b + 1, cp1);
+        if (!PLAIN) {
+            load_cols(seg, s, 2 * b, cp0);
+            load_cols(seg, s, 2 * b + 1, cp1);
+        }
         for (; i < g.M; i += GR) {
             r = reverse ? g.M - 1 - i : i;
             const uint16_t* xp = x + r * g.ldx + 16 * b;
             const uint4 v0 = ld16(xp), v1 = ld16(xp + 8);
-            if (r < seg_lo || r >= seg_hi) {
-                s = 0;
-                while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
-                seg_lo = seg.row_start[s];
-                seg_hi = seg.row_start[s + 1];
-                load_cols(seg, s, 2 * b, cp0);
-                load_cols(seg, s, 2 * b + 1, cp1);
-            }
             uint32_t y[8];
-            modulate8(v0, cp0, y);
-            modulate8(v1, cp1, y + 4);
+            if constexpr (PLAIN) {
+                y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
+                y[4] = v1.x; y[5] = v1.y; y[6] = v1.z; y[7] = v1.w;
+            } else {
+                if (r < seg_lo || r >= seg_hi) {
+                    s = 0;
+                    while (!(r >= seg.row_start[s] && r < seg.row_start[s + 1])) ++s;
+                    seg_lo = seg.row_start[s];
+                    seg_hi = seg.row_start[s + 1];
+                    load_cols(seg, s, 2 * b, cp0);
+                    load_cols(seg, s, 2 * b + 1, cp1);
+                }
+                modulate8(v0, cp0, y);
+                modulate8(v1, cp1, y + 4);
+            }
             pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + r * qld, sfa + r * sld, b);
         }
     }
@@ -627,6 +646,20 @@ __device__ __forceinline__ uint32_t block_amax_bits(float m, const float y[16]) 
     return a;
 }
 
+// The plain quantizer's y: the input itself, 16 columns as binary32 values,
+// and their largest magnitude (NaN if any value is NaN).
+__device__ __forceinline__ float plain16_f32(const uint4& a, const uint4& c, float y[16]) {
+    const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        y[2 * j] = bf16_lo(xw[j]);
+        y[2 * j + 1] = bf16_hi(xw[j]);
+        m = max_abs2(m, y[2 * j], y[2 * j + 1]);
+    }
+    return m;
+}
+
 // Scale and codes of one block given as binary32 values and the maximum from
 // mod16_f32; stores its 8 QDATA bytes and scale byte.
 __device__ __forceinline__ void pack16f_store(const float y[16], float m, float s_g, float rg, bool sg_fast,
@@ -718,6 +751,7 @@ __device__ __forceinline__ uint4 ld16o(const char* base, uint32_t off) {
 // end each iteration with a workgroup barrier: left to themselves the waves
 // of a workgroup drift apart by ~30 us over this loop and the last ones then
 // finish alone with too few loads in flight.
+template <bool PLAIN>
 __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const RowGeo& g, const SegParams& seg,
                                           const uint32_t (&hy)[kHoldRegs][8], const uint4* hold, const HoldSplit& hs,
                                           const float2* dr, float s_g, float rg, bool sg_fast, bool on, int r_first,
@@ -747,21 +781,26 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
     int s2 = 0;
     ColParams c0, c1;  // binary32 parameters: this loop is short of VALU, not of registers
     int seg_lo = 0;    // rows decrease in this loop
-    if (on) {
+    if (!PLAIN && on) {
         s2 = seg_find(seg, r_first + t * gstride, 0);
         load_cols(seg, s2, 2 * b, c0);
         load_cols(seg, s2, 2 * b + 1, c1);
         seg_lo = (int)seg.row_start[s2];
     }
     auto pack = [&](const uint4& v0, const uint4& v1, int r) {
-        if (r < seg_lo) {
-            s2 = seg_find(seg, r, s2);
-            seg_lo = (int)seg.row_start[s2];
-            load_cols(seg, s2, 2 * b, c0);
-            load_cols(seg, s2, 2 * b + 1, c1);
-        }
         float y[16];
-        const float m = mod16_f32(v0, v1, c0, c1, y);
+        float m;
+        if constexpr (PLAIN) {
+            m = plain16_f32(v0, v1, y);
+        } else {
+            if (r < seg_lo) {
+                s2 = seg_find(seg, r, s2);
+                seg_lo = (int)seg.row_start[s2];
+                load_cols(seg, s2, 2 * b, c0);
+                load_cols(seg, s2, 2 * b + 1, c1);
+            }
+            m = mod16_f32(v0, v1, c0, c1, y);
+        }
         pack16f_store(y, m, s_g, rg, sg_fast, dr, qdata + ((uint32_t)r * qrow + qcol), sfa + ((uint32_t)r * srow + b));
     };
     for (; t >= 1; t -= 2) {
@@ -780,6 +819,8 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
     }
 }
 
+// PLAIN: the plain quantizer (y = x, no modulation; seg is not read).
+template <bool PLAIN>
 __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                                  SegParams seg, uint32_t* ws, float* tensor_scale,
                                                                  float* amax_out, uint8_t* __restrict__ qdata,
@@ -806,21 +847,26 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         // (short of VALU here, not of registers: the held groups come later)
         ColParams c0, c1;
         int hi = 0, sc = 0;
-        if (on) {
+        if (!PLAIN && on) {
             sc = seg_find(seg, r_first < g.M ? r_first : 0, 0);
             load_cols(seg, sc, 2 * b, c0);
             load_cols(seg, sc, 2 * b + 1, c1);
             hi = (int)seg.row_start[sc + 1];
         }
         auto absmax = [&](const uint4& v0, const uint4& v1, int r) {
-            if (r >= hi) {
-                sc = seg_find(seg, r, sc);
-                hi = (int)seg.row_start[sc + 1];
-                load_cols(seg, sc, 2 * b, c0);
-                load_cols(seg, sc, 2 * b + 1, c1);
-            }
             uint32_t y[8];
-            mod16_packed(v0, v1, c0, c1, y);
+            if constexpr (PLAIN) {
+                y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
+                y[4] = v1.x; y[5] = v1.y; y[6] = v1.z; y[7] = v1.w;
+            } else {
+                if (r >= hi) {
+                    sc = seg_find(seg, r, sc);
+                    hi = (int)seg.row_start[sc + 1];
+                    load_cols(seg, sc, 2 * b, c0);
+                    load_cols(seg, sc, 2 * b + 1, c1);
+                }
+                mod16_packed(v0, v1, c0, c1, y);
+            }
             max16(m2, y);
         };
         for (; t + 1 < hs.ns; t += 2) {
@@ -844,12 +890,17 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             const uint4 a = ld16o(xb, o), c = ld16o(xb, o + 16);
             const uint32_t v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
             uint32_t y[8];
-            if (r >= seg_hi) {
-                s = seg_find(seg, r, s);
-                seg_hi = (int)seg.row_start[s + 1];
-                load_cols_pk(seg, s, b, cp);
+            if constexpr (PLAIN) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = v[k];
+            } else {
+                if (r >= seg_hi) {
+                    s = seg_find(seg, r, s);
+                    seg_hi = (int)seg.row_start[s + 1];
+                    load_cols_pk(seg, s, b, cp);
+                }
+                modulate16_pk(v, cp, y);
             }
-            modulate16_pk(v, cp, y);
             max16(m2, y);
             if (t >= hs.ns) hold_put(hold, t - hs.ns, y);
         }
@@ -872,16 +923,18 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         for (int h = 0; h < kHoldRegs; ++h) {
             const int r = r_first + (t0 + h) * gstride;
             const bool valid = h < hs.nr && r < g.M;
-            if (valid && r >= seg_hi) {
-                s = seg_find(seg, r, s);
-                seg_hi = (int)seg.row_start[s + 1];
-                load_cols_pk(seg, s, b, cp);
-            }
-            uint32_t y[8];
-            modulate16_pk(hy[h], cp, y);
+            if constexpr (!PLAIN) {
+                if (valid && r >= seg_hi) {
+                    s = seg_find(seg, r, s);
+                    seg_hi = (int)seg.row_start[s + 1];
+                    load_cols_pk(seg, s, b, cp);
+                }
+                uint32_t y[8];
+                modulate16_pk(hy[h], cp, y);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) hy[h][k] = y[k];
-            if (valid) max16(m2, y);
+                for (int k = 0; k < 8; ++k) hy[h][k] = y[k];
+            }
+            if (valid) max16(m2, hy[h]);
         }
     }
     const uint32_t bits = grid_max_barrier(fold_max(m2), ws, gen, tensor_scale, amax_out);
@@ -893,7 +946,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     const bool sg_fast = scale_in_fast_range(s_g);
     const float rg = 1.0f / s_g;
     zero_pad_rows(g, qdata, sfa);
-    pass2_mod(xb, g, seg, hy, hold, hs, dr, s_g, rg, sg_fast, on, r_first, gstride, b, qdata, sfa);
+    pass2_mod<PLAIN>(xb, g, seg, hy, hold, hs, dr, s_g, rg, sg_fast, on, r_first, gstride, b, qdata, sfa);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,16 +1020,24 @@ static int step_grid(int64_t n) {
 }
 
 hipError_t launch_modulate_absmax(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
-                                  float* tensor_scale, float* amax_out, hipStream_t s) {
-    hipLaunchKernelGGL(modulate_absmax_kernel, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws, tensor_scale,
-                       amax_out);
+                                  float* tensor_scale, float* amax_out, bool plain, hipStream_t s) {
+    if (plain)
+        hipLaunchKernelGGL(modulate_absmax_kernel<true>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws, tensor_scale,
+                           amax_out);
+    else
+        hipLaunchKernelGGL(modulate_absmax_kernel<false>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
+                           tensor_scale, amax_out);
     return hipGetLastError();
 }
 
 hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegParams& seg, const float* tensor_scale,
-                                uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
-    hipLaunchKernelGGL(modulate_pack_kernel, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, tensor_scale, qdata, sfa,
-                       g.reverse);
+                                uint8_t* qdata, uint8_t* sfa, bool plain, hipStream_t s) {
+    if (plain)
+        hipLaunchKernelGGL(modulate_pack_kernel<true>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, tensor_scale, qdata,
+                           sfa, g.reverse);
+    else
+        hipLaunchKernelGGL(modulate_pack_kernel<false>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, tensor_scale,
+                           qdata, sfa, g.reverse);
     return hipGetLastError();
 }
 
@@ -1005,7 +1066,8 @@ static int resident_grid(const void* kernel, int* cache) {
 int modulate_quantize_grid() {
     static int cache[kMaxDevices] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
                                      -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
-    return resident_grid((const void*)modulate_quantize_kernel, cache);
+    // both instantiations have the same resources (the held rows fill the registers and LDS)
+    return resident_grid((const void*)modulate_quantize_kernel<false>, cache);
 }
 
 // A plain launch: the grid never exceeds what the device holds at once, so on
@@ -1013,11 +1075,15 @@ int modulate_quantize_grid() {
 // barrier completes (its wait is bounded in any case).  The cooperative launch
 // API would guarantee residency but costs tens of microseconds per launch.
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
-                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                    float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
                                     hipStream_t s) {
     const int hold_lds = kModHoldLdsBytes / (32 * g.block);
-    hipLaunchKernelGGL(modulate_quantize_kernel, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws, tensor_scale,
-                       amax_out, qdata, sfa, hold_lds);
+    if (plain)
+        hipLaunchKernelGGL(modulate_quantize_kernel<true>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
+                           tensor_scale, amax_out, qdata, sfa, hold_lds);
+    else
+        hipLaunchKernelGGL(modulate_quantize_kernel<false>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
+                           tensor_scale, amax_out, qdata, sfa, hold_lds);
     return hipGetLastError();
 }
 

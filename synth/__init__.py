@@ -35,7 +35,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
-T_X, T_SHIFT, T_SCALE, T_WEIGHT, T_OUT_MASK, T_OUT_VAL, T_ROWS = range(7)
+T_X, T_SHIFT, T_SCALE, T_WEIGHT, T_OUT_MASK, T_OUT_VAL, T_ROWS, T_GATE, T_RESIDUAL = range(9)
 
 
 def build(verbose: bool = False) -> str:
@@ -119,7 +119,8 @@ def sample_rows(c: int, M: int, k: int, must=()) -> np.ndarray:
 
 @dataclass
 class Workload:
-    """One synthetic configuration.  ``kind`` is 'modulate' or 'swiglu'."""
+    """One synthetic configuration.  ``kind`` is 'modulate', 'swiglu' or
+    'plain' (quantized without modulation)."""
     name: str
     kind: str
     M: int
@@ -141,8 +142,8 @@ class Workload:
         return (self.M + 63) // 64 * 64
 
     def x(self) -> np.ndarray:
-        """Modulation input [M, K] bf16 bits."""
-        assert self.kind == "modulate"
+        """Producer input [M, K] bf16 bits (modulation or plain quantizer)."""
+        assert self.kind in ("modulate", "plain")
         a = normal_bf16(self.c_x, T_X, (self.M, self.K), self.x_sigma)
         self._outliers(a, self.c_x)
         if self.zero_block:
@@ -179,6 +180,20 @@ class Workload:
         assert self.N is not None
         return normal_bf16(self.c_w, T_WEIGHT, (self.N, self.K), self.w_sigma)
 
+    def gates(self):
+        """(row_start int64 [S+1], gate [S, N]) bf16 bits for the residual
+        epilogue: gates ~ N(1, seg_sigma) per segment and output column."""
+        S = len(self.row_start) - 1
+        g = normal_bf16(self.c_seg, T_GATE, (S, self.N), self.seg_sigma)
+        # gate = 1 + N(0, sigma): shift the binary32 values by 1, then round to
+        # bf16 (nearest, ties to even; every value here is finite)
+        u = ((g.astype(np.uint32) << 16).view(np.float32) + np.float32(1.0)).view(np.uint32)
+        return np.array(self.row_start, np.int64), ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+    def residual(self) -> np.ndarray:
+        """Residual stream [M, N] bf16 bits, N(0, 1)."""
+        return normal_bf16(self.c_seg, T_RESIDUAL, (self.M, self.N), 1.0)
+
     def check_rows(self, k: int = 64) -> np.ndarray:
         """GEMM rows checked at full size: boundary rows plus seeded rows."""
         return sample_rows(self.c_x, self.M, k, self.boundary_rows)
@@ -202,6 +217,11 @@ WORKLOADS = {
                     boundary_rows=_BOUNDARY),
     "fc2": Workload("fc2", "swiglu", M_CANON, 14336, 5376, c_x=5, c_w=5, w_sigma=0.01,
                     boundary_rows=_BOUNDARY),
+    # attention output: attention values [M, 7168] through the plain quantizer,
+    # projected to the model width 5376 with the residual epilogue
+    "attn_out": Workload("attn_out", "plain", M_CANON, 7168, 5376, c_x=6, c_seg=6, c_w=6, w_sigma=0.02,
+                         row_start=(0, 31000, M_CANON), outliers=("t3", 0.001, 20.0),
+                         boundary_rows=_BOUNDARY),
 }
 
 

@@ -22,10 +22,18 @@ def _map(fn, items):
         return list(ex.map(fn, items))
 
 
+def amax_merge(values):
+    """Maximum of per-range maxima (non-negative bf16 magnitudes, NaN possible)
+    as the oracle takes it: over bit patterns, so NaN ranks above Inf above
+    every finite value (Python's max() would drop a NaN depending on order)."""
+    bits = np.array([np.float32(v) for v in values], np.float32).view(np.uint32)
+    return float(bits.max().view(np.float32))
+
+
 def modulate_quantize(x, seg, m_pad):
     M = x.shape[0]
     x = np.ascontiguousarray(x)
-    amax = max(_map(lambda r: oracle.modulate_amax_rows(x, seg, *r), _ranges(M, 4 * WORKERS)))
+    amax = amax_merge(_map(lambda r: oracle.modulate_amax_rows(x, seg, *r), _ranges(M, 4 * WORKERS)))
     s_g = oracle.tensor_scale(amax)
     parts = _map(lambda r: oracle.modulate_pack_rows(x, seg, s_g, *r), _ranges(m_pad, 4 * WORKERS))
     return (np.float32(s_g), np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
@@ -42,7 +50,7 @@ def modulate_pack(x, seg, s_g, r0, r1):
 def swiglu_quantize(gu, m_pad):
     M = gu.shape[0]
     gu = np.ascontiguousarray(gu)
-    amax = max(_map(lambda r: oracle.swiglu_amax_rows(gu, *r), _ranges(M, 4 * WORKERS)))
+    amax = amax_merge(_map(lambda r: oracle.swiglu_amax_rows(gu, *r), _ranges(M, 4 * WORKERS)))
     s_g = oracle.tensor_scale(amax)
     parts = _map(lambda r: oracle.swiglu_pack_rows(gu, s_g, *r), _ranges(m_pad, 4 * WORKERS))
     return (np.float32(s_g), np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
@@ -60,7 +68,7 @@ def quantize_bf16(y, m_pad=None):
     M = y.shape[0]
     m_pad = M if m_pad is None else m_pad
     y = np.ascontiguousarray(y)
-    amax = max(_map(lambda r: oracle.bf16_amax(y[r[0]:r[1]]), _ranges(M, 4 * WORKERS)))
+    amax = amax_merge(_map(lambda r: oracle.bf16_amax(y[r[0]:r[1]]), _ranges(M, 4 * WORKERS)))
     s_g = oracle.tensor_scale(amax)
     parts = _map(lambda r: oracle.bf16_pack_rows(y, s_g, *r), _ranges(m_pad, 4 * WORKERS))
     return (np.float32(s_g), np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),

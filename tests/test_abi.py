@@ -120,6 +120,11 @@ def test_producer_argument_errors(pkg):
     assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, None, q, s, 32, None) == 2            # M_pad
     assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, None, q + 1, s, 64, None) == 3        # qdata
     assert mq(FAKE, 10, 64, 64, ctypes.byref(seg), ws, ts, FAKE + 2, q, s, 64, None) == 3        # amax_out
+    assert L.nvfp4_quantize(None, 10, 64, 64, ws, ts, None, q, s, 64, None) == 1
+    assert L.nvfp4_quantize(FAKE, 10, 40, 40, ws, ts, None, q, s, 64, None) == 2           # D % 16
+    assert L.nvfp4_quantize(FAKE, 10, 64, 64, None, ts, None, q, s, 64, None) == 1         # workspace
+    assert L.nvfp4_quantize(FAKE, 10, 64, 64, ws, ts, None, q, s, 32, None) == 2           # M_pad
+    assert L.nvfp4_quantize(FAKE, 10, 64, 64, ws, ts, None, q + 2, s, 64, None) == 3       # qdata
     assert L.nvfp4_swiglu_absmax(FAKE, FAKE, 10, 24, 48, ws, ts, None, None) == 2
     assert L.nvfp4_swiglu_pack(FAKE, None, 10, 32, 64, ts, q, s, 64, None) == 1
 

@@ -182,11 +182,11 @@ def test_canonical_projection_sampled_rows(m, name):
     # checked rows, its own weight quantization
     if w.kind == "modulate":
         seg = oracle.Segments(rs, sh, sc)
-        amax = max(_par._map(lambda r: oracle.modulate_amax_rows(x, seg, *r), _par._ranges(w.M, 64)))
+        amax = _par.amax_merge(_par._map(lambda r: oracle.modulate_amax_rows(x, seg, *r), _par._ranges(w.M, 64)))
         sa = oracle.tensor_scale(amax)
         parts = _par._map(lambda r: oracle.modulate_pack_rows(x, seg, sa, r, r + 1), list(rows))
     else:
-        amax = max(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(w.M, 64)))
+        amax = _par.amax_merge(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(w.M, 64)))
         sa = oracle.tensor_scale(amax)
         parts = _par._map(lambda r: oracle.swiglu_pack_rows(gu, sa, r, r + 1), list(rows))
     assert np.float32(sa) == host(ts)[0]
@@ -380,3 +380,45 @@ def test_gate_residual_random_within_tolerance(m):
     bound = e_g + 2.0 ** -8 * (np.abs(ref) + e_g) + 1e-30
     err = np.abs(got - ref)
     assert np.all(err <= bound), float(np.max(err / bound))
+
+
+def test_attention_output_projection_with_residual_epilogue(m):
+    """The attention-output projection at M = 37,810, K = 7,168, N = 5,376: the
+    plain quantizer, then the GEMM with the residual epilogue (two segments of
+    gates).  The packed activation is compared byte for byte with the oracle's
+    on the checked rows, the outputs against the FP64 reference
+    residual + gate * ref within the tolerance of the epilogue test above."""
+    w = synth.workload("attn_out")
+    dev = device()
+    x = w.x()
+    W = w.weight()
+    rs, gate = w.gates()
+    residual = w.residual()
+    print(f"attn_out: M={w.M} K={w.K} N={w.N}", flush=True)
+    q, s, ts, _ = m.quantize(to_dev_u16(x))
+    qw, sfw, tw = m.quantize_weight(to_dev_u16(W))
+    res = to_dev_u16(residual)
+    gates, keep = m.make_row_gates(rs, to_dev_u16(gate))
+    need = m.nvfp4_gemm_workspace_bytes(w.M, w.N, w.K)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    m.nvfp4_gemm_gate_residual(q, s, ts, w.M, q.shape[0], qw, sfw, tw, w.N, w.K, gates, res, w.N, res, w.N, ws,
+                               need)
+    torch.cuda.synchronize()
+    rows = w.check_rows(64)
+    sa, oqa, osfa, _ = _par.quantize_bf16(x, w.m_pad)
+    assert np.float32(sa) == host(ts)[0]
+    assert np.array_equal(host(q)[rows], oqa[rows]) and np.array_equal(host(s)[rows], osfa[rows])
+    sw, oqw, osfw, _ = _par.quantize_bf16(W)
+    assert sw == host(tw)[0]
+    ref_o = _par.gemm_rows(oqa, osfa, sa, oqw, osfw, sw, rows)
+    seg = np.searchsorted(rs[1:], rows, side="right")
+    g = (gate.astype(np.uint32) << 16).view(np.float32).astype(np.float64)[seg]
+    r = (residual[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = r + g * ref_o
+    got = out_f64(res[torch.from_numpy(rows).to(dev)])
+    e_o = 2.0 ** -7 * np.abs(ref_o) + 1e-3 * np.sqrt(np.mean(ref_o ** 2))
+    e_g = np.abs(g) * e_o + 2.0 ** -8 * np.abs(g) * (np.abs(ref_o) + e_o)
+    bound = e_g + 2.0 ** -8 * (np.abs(ref) + e_g) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    del keep

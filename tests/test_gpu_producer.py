@@ -244,6 +244,55 @@ def test_weight_prepack_matches_oracle_quantizer(m):
 
 
 # --------------------------------------------------------------------------
+# Plain quantizer (no modulation)
+# --------------------------------------------------------------------------
+def check_plain(m, y, m_pad=None, nan_ok=False):
+    M = y.shape[0]
+    m_pad = oracle.padded_rows(M) if m_pad is None else m_pad
+    s_g, q, s, amax = _par.quantize_bf16(y, m_pad)
+    gq, gs, gts, gamax = m.quantize(to_dev_u16(y), m_pad=m_pad)
+    torch.cuda.synchronize()
+    ga, gt = np.float32(host(gamax)[0]), np.float32(host(gts)[0])
+    if nan_ok and np.isnan(amax):
+        assert np.isnan(ga) and np.isnan(gt)
+        # the maximum is the largest magnitude bit pattern, NaN payload included
+        assert (ga.view(np.uint32) >> 16) & 0x7FFF == (np.float32(amax).view(np.uint32) >> 16) & 0x7FFF
+    else:
+        assert ga.view(np.uint32) == np.float32(amax).view(np.uint32) and gt == np.float32(s_g)
+    assert np.array_equal(host(gs), s), "SFA " + str(first_mismatch(host(gs), s))
+    assert np.array_equal(host(gq), q), "QDATA " + str(first_mismatch(host(gq), q))
+
+
+@pytest.mark.parametrize("M,D", [(1, 16), (63, 48), (769, 5376), (130, 8208), (21, 16400), (300, 7168)])
+def test_plain_quantizer_shapes(m, M, D):
+    rng = np.random.default_rng(M * 3 + D)
+    y = bf16_np(rng.standard_normal((M, D)) * np.where(rng.random((M, D)) < 0.01, 100.0, 1.0))
+    check_plain(m, y)
+
+
+def test_plain_quantizer_every_bf16_value_and_nan(m):
+    """All 65,536 bf16 patterns, NaN included: the plain quantizer passes NaN
+    through, the maximum is NaN and every block gets the NaN scale code."""
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    y = vals.reshape(128, 512)
+    check_plain(m, y, nan_ok=True)
+    finite = vals[(vals & 0x7FFF) < 0x7F80]
+    D = 512
+    rows = (finite.size + D - 1) // D
+    y2 = np.concatenate([finite, np.zeros(rows * D - finite.size, np.uint16)]).reshape(rows, D)
+    check_plain(m, y2)
+
+
+def test_plain_quantizer_attention_output_canonical(m):
+    """The attention-output activation [37810, 7168] through the plain
+    quantizer, every row byte-exact."""
+    w = synth.workload("attn_out")
+    x = w.x()
+    print(f"attn_out activation {x.shape}", flush=True)
+    check_plain(m, x)
+
+
+# --------------------------------------------------------------------------
 # SwiGLU producer
 # --------------------------------------------------------------------------
 def check_swiglu(m, gu, m_pad=None):
@@ -305,7 +354,7 @@ def test_swiglu_canonical_37810_rows(m):
     print(f"swiglu workload {gu.shape}", flush=True)
     gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu))
     torch.cuda.synchronize()
-    amax = max(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(M, 64)))
+    amax = _par.amax_merge(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(M, 64)))
     s_g = oracle.tensor_scale(amax)
     assert host(gamax)[0] == amax and host(gts)[0] == np.float32(s_g)
     rows = np.unique(np.concatenate([synth.sample_rows(5, M, 2048, w.boundary_rows), np.arange(M, w.m_pad)]))

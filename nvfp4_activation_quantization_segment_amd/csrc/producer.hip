@@ -342,7 +342,7 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
 // groups, the workgroups meet at a grid barrier where the global maximum is
 // complete, and pass 2 follows in the same launch.  The y values of the row
 // groups a workgroup visited last stay on chip across the barrier: the last
-// kHoldRegs groups in registers, the ones before them in LDS; pass 2 packs
+// hold_regs() groups in registers, the ones before them in LDS; pass 2 packs
 // those first and then reads only the remaining rows from memory again, last
 // to first.  The grid never exceeds the workgroups the device holds at once
 // (one per CU: the held rows fill the LDS), so the barrier completes on a
@@ -352,7 +352,9 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
 // Thread layout as in the pack passes: thread idx takes block idx % C16 of row
 // offset idx / C16 in a group of R rows; workgroup w visits groups w, w+G, ...
 // ---------------------------------------------------------------------------
-constexpr int kHoldRegs = 7;                 // row groups held in registers per thread
+// Row groups held in registers per thread: as many as fit in 128 VGPRs beside
+// the working set without spills (the modulation keeps column parameters live).
+constexpr int hold_regs(bool plain) { return plain ? 11 : 7; }
 constexpr int kModHoldLdsBytes = 152 * 1024;  // LDS for held groups (modulation)
 constexpr uint64_t kBarrierTicks = 100000000;  // wait bound: 1 s of the 100 MHz real-time counter
 
@@ -554,11 +556,11 @@ __device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, uint64_t gen, f
 struct HoldSplit {
     int ns, nl, nr;
 };
-__device__ __forceinline__ HoldSplit hold_split(int64_t groups, int hold_lds) {
+__device__ __forceinline__ HoldSplit hold_split(int64_t groups, int hold_lds, int hold_reg) {
     const int64_t G = gridDim.x, w = blockIdx.x;
     const int nw = w < groups ? (int)((groups - 1 - w) / G + 1) : 0;
     HoldSplit h;
-    h.nr = nw < kHoldRegs ? nw : kHoldRegs;
+    h.nr = nw < hold_reg ? nw : hold_reg;
     h.nl = (nw - h.nr) < hold_lds ? (nw - h.nr) : hold_lds;
     h.ns = nw - h.nr - h.nl;
     return h;
@@ -751,9 +753,9 @@ __device__ __forceinline__ uint4 ld16o(const char* base, uint32_t off) {
 // end each iteration with a workgroup barrier: left to themselves the waves
 // of a workgroup drift apart by ~30 us over this loop and the last ones then
 // finish alone with too few loads in flight.
-template <bool PLAIN>
+template <bool PLAIN, int HR = hold_regs(PLAIN)>
 __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const RowGeo& g, const SegParams& seg,
-                                          const uint32_t (&hy)[kHoldRegs][8], const uint4* hold, const HoldSplit& hs,
+                                          const uint32_t (&hy)[HR][8], const uint4* hold, const HoldSplit& hs,
                                           const float2* dr, float s_g, float rg, bool sg_fast, bool on, int r_first,
                                           int gstride, int b, uint8_t* __restrict__ qdata,
                                           uint8_t* __restrict__ sfa) {
@@ -763,7 +765,7 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
     const int t0 = hs.ns + hs.nl;
     if (on) {
 #pragma unroll
-        for (int h = 0; h < kHoldRegs; ++h) {
+        for (int h = 0; h < HR; ++h) {
             const int r = r_first + (t0 + h) * gstride;
             if (h < hs.nr && r < g.M)
                 pack_block16_store(hy[h], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
@@ -832,7 +834,8 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     const int rho = threadIdx.x / C16, b = threadIdx.x - rho * C16;
     const bool on = rho < g.R;
     const int64_t groups = (g.M + g.R - 1) / g.R;
-    const HoldSplit hs = hold_split(groups, hold_lds);
+    constexpr int HR = hold_regs(PLAIN);
+    const HoldSplit hs = hold_split(groups, hold_lds, HR);
     const int gstride = (int)gridDim.x * g.R;
     const int r_first = (int)blockIdx.x * g.R + rho;  // row of local group 0
     const uint32_t xrow = 2u * (uint32_t)g.ldx, xcol = 32u * (uint32_t)b;
@@ -840,7 +843,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
 
     // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
     uint32_t m2 = 0;
-    uint32_t hy[kHoldRegs][8];
+    uint32_t hy[HR][8];
     int t = 0;
     {
         // streamed groups, two per iteration, with binary32 column parameters
@@ -907,7 +910,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         // register-held groups: all loads first, then y in place of x
         const int t0 = hs.ns + hs.nl;
 #pragma unroll
-        for (int h = 0; h < kHoldRegs; ++h) {
+        for (int h = 0; h < HR; ++h) {
             const int r = r_first + (t0 + h) * gstride;
             if (h < hs.nr && r < g.M) {
                 const uint32_t o = (uint32_t)r * xrow + xcol;
@@ -920,7 +923,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             }
         }
 #pragma unroll
-        for (int h = 0; h < kHoldRegs; ++h) {
+        for (int h = 0; h < HR; ++h) {
             const int r = r_first + (t0 + h) * gstride;
             const bool valid = h < hs.nr && r < g.M;
             if constexpr (!PLAIN) {

@@ -459,16 +459,25 @@ def _gemm_role(name):
 def _gemm_calls(items):
     """Group GEMM dispatches (in dispatch order) into calls: a main launch
     starts a call, split and finalize launches belong to the call before them.
-    items: (dispatch_id, kernel_name, payload).  Returns [(projection, [payloads])]."""
+    items: (dispatch_id, kernel_name, grid, payload).  The step's calls cycle
+    through QKV, FC1, FC2, each with its own main-launch grid; the grids are
+    taken from the first three calls and the grouping stops at the first call
+    that breaks the cycle (the attention-output projection timed after the
+    steps).  Returns [(projection, [payloads])]."""
     calls = []
-    for _, name, payload in sorted(items, key=lambda t: t[0]):
+    for _, name, grid, payload in sorted(items, key=lambda t: t[0]):
         role = _gemm_role(name)
         if role is None:
             continue
         if role == "main" or not calls:
-            calls.append([])
-        calls[-1].append(payload)
-    return [(PROJ[i % 3], c) for i, c in enumerate(calls)]
+            calls.append((grid, []))
+        calls[-1][1].append(payload)
+    out = []
+    for i, (grid, c) in enumerate(calls):
+        if i >= 3 and grid != calls[i % 3][0]:
+            break
+        out.append((PROJ[i % 3], c))
+    return out
 
 
 def _csv_rows(d, suffix):
@@ -500,7 +509,7 @@ def summarize_trace(d):
             continue
         out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-    calls = _gemm_calls([(int(r["Dispatch_Id"]), r["Kernel_Name"],
+    calls = _gemm_calls([(int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size_X"]),
                           (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace])
     per = {p: [] for p in PROJ}
     for p, c in calls:
@@ -557,9 +566,9 @@ def summarize_traffic(fetch_dir, write_dir):
     w = {k: e for k, e in w.items() if k > w0}
 
     per = {p: {"fetch": [], "write": []} for p in PROJ}
-    for p, c in _gemm_calls([(k, e["name"], e["v"]) for k, e in f.items()]):
+    for p, c in _gemm_calls([(k, e["name"], e["grid"], e["v"]) for k, e in f.items()]):
         per[p]["fetch"].append(sum(c) * fs * 1024)
-    for p, c in _gemm_calls([(k, e["name"], e["v"]) for k, e in w.items()]):
+    for p, c in _gemm_calls([(k, e["name"], e["grid"], e["v"]) for k, e in w.items()]):
         per[p]["write"].append(sum(c) * ws * 1024)
     shapes = {}
     for p in PROJ:
@@ -613,7 +622,8 @@ def summarize_traffic(fetch_dir, write_dir):
 def summarize_counters(d):
     """Mean of each counter per kernel (dispatches grouped by kernel name and
     grid), with the elements one launch covers for the producer kernels of the
-    step: modulation [37810, 5376], SwiGLU output [37810, 14336]."""
+    step: modulation [37810, 5376], SwiGLU output [37810, 14336], and for the
+    plain quantizer of the attention-output projection [37810, 7168]."""
     import numpy as np
 
     rows = _csv_rows(d, "counter_collection.csv")
@@ -627,13 +637,14 @@ def summarize_counters(d):
         if "nvfp4::" in e["name"]:
             groups.setdefault((e["name"].replace("nvfp4::", ""), e["grid"]), []).append(e)
     names = sorted({c for e in by.values() for c in e if c not in ("name", "grid")})
-    elems = {"modulate": 37810 * 5376, "swiglu": 37810 * 14336}
+    elems = {"modulate": 37810 * 5376, "plain": 37810 * 7168, "swiglu": 37810 * 14336}
     out = ["| kernel | grid | dispatches | " + " | ".join(names) + " | VALU lane-ops / element |",
            "|---|---|---|" + "---|" * len(names) + "---|"]
     for (n, g), es in sorted(groups.items(), key=lambda t: -len(t[1])):
         means = [float(np.mean([e.get(c, 0.0) for e in es])) for c in names]
         # the step's producer launches: 256 workgroups of 1024 (modulation) or 896 (SwiGLU) threads
-        kind = ("modulate" if "modulate" in n and g == 256 * 1024 else
+        kind = ("modulate" if "modulate_quantize_kernel<false>" in n and g == 256 * 1024 else
+                "plain" if "modulate_quantize_kernel<true>" in n and g == 256 * 1024 else
                 "swiglu" if "swiglu" in n and "fill" not in n and g == 256 * 896 else None)
         per = ""
         if kind and "SQ_INSTS_VALU" in names:
@@ -655,11 +666,11 @@ def summarize_mfma(d):
     for r in rows:
         if _gemm_role(r["Kernel_Name"]) is None:
             continue
-        e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+        e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
                                                  "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     per = {p: [] for p in PROJ}
-    for p, c in _gemm_calls([(k, e["name"], e) for k, e in by.items()]):
+    for p, c in _gemm_calls([(k, e["name"], e["grid"], e) for k, e in by.items()]):
         tot = {"us": sum(x["us"] for x in c)}
         for key in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES"):
             tot[key] = sum(x.get(key, 0.0) for x in c)

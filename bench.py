@@ -239,6 +239,9 @@ def main():
         for i, (label, _, _) in enumerate(seq):
             per[label].append(evs[k][i].elapsed_time(evs[k][i + 1]))
     med = {label: float(np.median(v)) for label, v in per.items()}
+    launch_pct = {label: {"p50": round(float(np.percentile(v, 50)), 4), "p95": round(float(np.percentile(v, 95)), 4)}
+                  for label, v in per.items()}
+    standalone = standalone_producers(seq, stream, dev, reps=20)
 
     # algorithmic work
     def mod_bytes(K):  # two reads of x + QDATA + SFA written (padded rows included)
@@ -309,7 +312,13 @@ def main():
             for nme in flops
         },
         "timing": {"wall_ms_timed_region": round(wall_ms, 2), "event_ms_timed_region": round(total_ms, 2),
-                   "setup_s": round(setup_s, 1), "kernel_source_hash": gemm_hash},
+                   "setup_s": round(setup_s, 1), "kernel_source_hash": gemm_hash,
+                   "launch_ms_in_step": launch_pct},
+        "producer_standalone": {
+            nme: dict(v, bytes=prod_bytes[nme],
+                      frac_hbm_cold_p50=round(prod_bytes[nme] / (v["cold_p50_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+            for nme, v in standalone.items()
+        },
         "context": "pages' numbers (GB10/DGX Spark): fused producer 6.02 ms for the block-24 QKV input vs "
                    "10.47/10.60 ms unfused modulation; CUTLASS 1024^3 block-scaled GEMM 126.57 TFLOP/s",
         "cpu_baseline": None,
@@ -320,6 +329,50 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, x_h, segs, gu_h, (wq, wf1, wf2))
     print(json.dumps(result), flush=True)
+
+
+def standalone_producers(seq, stream, dev, reps):
+    """Each producer of the step timed on its own (after the timed steps):
+    cold = right after a 1 GiB read of another buffer, which evicts the input
+    from every cache level (a read, not a write: written lines would still be
+    dirty in the memory-side cache and their write-back would be timed with the
+    producer), warm = run again straight after itself.  HIP events on the launch
+    stream; p50 and p95 over `reps`."""
+    import numpy as np
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    parts = {}
+    for label, _, fn in seq:
+        nme, part = label.split(".")
+        if part != "gemm":
+            parts.setdefault(nme, []).append(fn)
+    out = {}
+    for nme, fns in parts.items():
+        cold, warm = [], []
+        for k in range(reps + 1):  # the first rep is a warm-up
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            with torch.cuda.stream(stream):
+                flush.max()
+            ev[0].record(stream)
+            for fn in fns:
+                fn()
+            ev[1].record(stream)
+            ev[2].record(stream)
+            for fn in fns:
+                fn()
+            ev[3].record(stream)
+            stream.synchronize()
+            if k:
+                cold.append(ev[0].elapsed_time(ev[1]))
+                warm.append(ev[2].elapsed_time(ev[3]))
+        out[nme] = {"cold_p50_ms": round(float(np.percentile(cold, 50)), 4),
+                    "cold_p95_ms": round(float(np.percentile(cold, 95)), 4),
+                    "warm_p50_ms": round(float(np.percentile(warm, 50)), 4),
+                    "warm_p95_ms": round(float(np.percentile(warm, 95)), 4)}
+    del flush
+    return out
 
 
 def attn_out_projection(nv, synth, dev, stream, reps):

@@ -366,3 +366,95 @@ def test_swiglu_canonical_37810_rows(m):
         s = np.concatenate([p[1] for p in parts])
         assert np.array_equal(gs_h[rr], s), first_mismatch(gs_h[rr], s)
         assert np.array_equal(gq_h[rr], q), first_mismatch(gq_h[rr], q)
+
+
+# Inputs past 4 GiB: byte offsets beyond 2^32, where the producers leave the
+# single launch and 32-bit offsets for the two passes with 64-bit offsets.
+# The rows repeat a seeded block of 61 rows (a period that no tiling of the
+# kernels divides), built on the device; the oracle runs on the block.
+_P = 61
+
+
+def _tiled_dev(block, M):
+    b = to_dev_u16(block)
+    return b.repeat(-(-M // _P), 1)[:M].contiguous()
+
+
+def _rows_past_4gib(c, M, row_bytes, must):
+    """Sampled rows over the whole range, most of them past byte 2^32."""
+    first = -(-(1 << 32) // row_bytes)
+    lo = synth.sample_rows(c, first, 48, must=[r for r in must if r < first])
+    hi = first + synth.sample_rows(c + 1, M - first, 160, must=[r - first for r in must if r >= first])
+    return np.unique(np.concatenate([lo, hi]))
+
+
+def test_modulation_and_plain_inputs_past_4_gib(m):
+    """x [400,000, 5,376] bf16 (4.30 GB), two segments: tensor scale, QDATA and
+    SFA of sampled rows (incl. both sides of the segment boundary and the last
+    row) and every padding row, for the modulation producer and the plain
+    quantizer."""
+    M, D = 400_000, 5376
+    assert (M - 1) * D * 2 >= 1 << 32
+    boundary = 250_001
+    block = synth.add_outliers_t3(synth.normal_bf16(40, 0, (_P, D), 1.0), 40, 0.001, 20.0)
+    sh = synth.normal_bf16(41, 1, (2, D), 0.1)
+    sc = synth.normal_bf16(41, 2, (2, D), 0.1)
+    rs = [0, boundary, M]
+    print(f"x [{M}, {D}] tiled from {_P} rows on the device", flush=True)
+    x = _tiled_dev(block, M)
+    q, s, ts, amax = m.modulate_quantize(x, rs, to_dev_u16(sh), to_dev_u16(sc))
+    torch.cuda.synchronize()
+    # every row phase occurs in both segments, so the global maximum is the
+    # block's maximum under either segment's parameters
+    seg2 = oracle.Segments([0, _P, 2 * _P], sh, sc)
+    oamax = oracle.modulate_amax_rows(np.concatenate([block, block]), seg2, 0, 2 * _P)
+    s_g = np.float32(oracle.tensor_scale(oamax))
+    assert np.float32(host(amax)[0]).view(np.uint32) == np.float32(oamax).view(np.uint32)
+    assert host(ts)[0].view(np.uint32) == s_g.view(np.uint32)
+    rows = _rows_past_4gib(42, M, D * 2, [0, boundary - 1, boundary, M - 1])
+    n0 = int(np.searchsorted(rows, boundary))
+    assert 0 < n0 < rows.size
+    oq, os_ = oracle.modulate_pack_rows(block[rows % _P], oracle.Segments([0, n0, rows.size], sh, sc), s_g,
+                                        0, rows.size)
+    ridx = torch.from_numpy(rows).to(x.device)
+    gq, gs = host(q[ridx]), host(s[ridx])
+    assert np.array_equal(gs, os_), first_mismatch(gs, os_)
+    assert np.array_equal(gq, oq), first_mismatch(gq, oq)
+    assert not host(q[M:]).any() and not host(s[M:]).any()
+    del q, s
+
+    print("plain quantizer on the same x", flush=True)
+    q, s, ts, amax = m.quantize(x)
+    torch.cuda.synchronize()
+    pamax = oracle.bf16_amax(block)
+    ps_g = np.float32(oracle.tensor_scale(pamax))
+    assert host(ts)[0].view(np.uint32) == ps_g.view(np.uint32)
+    oq, os_ = oracle.bf16_pack_rows(block[rows % _P], ps_g, 0, rows.size)
+    gq, gs = host(q[ridx]), host(s[ridx])
+    assert np.array_equal(gs, os_), first_mismatch(gs, os_)
+    assert np.array_equal(gq, oq), first_mismatch(gq, oq)
+    assert not host(q[M:]).any() and not host(s[M:]).any()
+
+
+def test_swiglu_input_past_4_gib(m):
+    """gate/up [80,000, 2*14,336] bf16 (4.59 GB; the pack pass's 64-bit offset
+    variant): tensor scale, QDATA and SFA of sampled rows and every padding
+    row."""
+    M, F = 80_000, 14_336
+    assert (M - 1) * 2 * F * 2 >= 1 << 32
+    block = synth.normal_bf16(43, 0, (_P, 2 * F), 1.0)
+    print(f"gate/up [{M}, {2 * F}] tiled from {_P} rows on the device", flush=True)
+    gu = _tiled_dev(block, M)
+    q, s, ts, amax = m.swiglu_quantize(gu)
+    torch.cuda.synchronize()
+    oamax = oracle.swiglu_amax_rows(block, 0, _P)
+    s_g = np.float32(oracle.tensor_scale(oamax))
+    assert np.float32(host(amax)[0]).view(np.uint32) == np.float32(oamax).view(np.uint32)
+    assert host(ts)[0].view(np.uint32) == s_g.view(np.uint32)
+    rows = _rows_past_4gib(44, M, 4 * F, [0, M - 1])
+    oq, os_ = oracle.swiglu_pack_rows(block[rows % _P], s_g, 0, rows.size)
+    ridx = torch.from_numpy(rows).to(gu.device)
+    gq, gs = host(q[ridx]), host(s[ridx])
+    assert np.array_equal(gs, os_), first_mismatch(gs, os_)
+    assert np.array_equal(gq, oq), first_mismatch(gq, oq)
+    assert not host(q[M:]).any() and not host(s[M:]).any()

@@ -421,20 +421,42 @@ gemm_kernel(GemmArgs a, GemmPart p) {
         __syncthreads();
         const int n = tn * kBN + wn * kWN + (lane & 7) * 8;
         const int m0 = tm * kBM + wm * kWM + (lane >> 3);
-        if (n < a.N) {
+        if (n < a.N && !a.epi) {
+#pragma unroll
+            for (int it = 0; it < kWM / 8; ++it) {
+                const int m = m0 + 8 * it;
+                if (m < a.M) {
+                    const uint4 v =
+                        *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
+                    store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
+                }
+            }
+        } else if (n < a.N) {
+            // Residual epilogue: all 16 residual loads of the lane first (rows
+            // past M clamped to the last row, never stored), and one gate
+            // vector when the wave's 128 rows lie in one segment, so that the
+            // load latency is paid once rather than once per row.
+            const int wfirst = tm * kBM + wm * kWM;
+            const int wlast = wfirst + kWM - 1 < a.M - 1 ? wfirst + kWM - 1 : a.M - 1;
+            const uint16_t* g_first = gate_row(a, wfirst < a.M ? wfirst : a.M - 1);
+            const bool one_gate = g_first == gate_row(a, wlast);
+            const uint4 g_wave = *reinterpret_cast<const uint4*>(g_first + n);
+            uint4 res[kWM / 8];
+#pragma unroll
+            for (int it = 0; it < kWM / 8; ++it) {
+                const int m = m0 + 8 * it < a.M ? m0 + 8 * it : a.M - 1;
+                res[it] = *reinterpret_cast<const uint4*>(a.residual + (int64_t)m * a.ldr + n);
+            }
 #pragma unroll
             for (int it = 0; it < kWM / 8; ++it) {
                 const int m = m0 + 8 * it;
                 if (m < a.M) {
                     uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
-                    if (a.epi) {
-                        const uint4 g = *reinterpret_cast<const uint4*>(gate_row(a, m) + n);
-                        const uint4 r = *reinterpret_cast<const uint4*>(a.residual + (int64_t)m * a.ldr + n);
-                        v.x = gate_residual2(v.x, g.x, r.x);
-                        v.y = gate_residual2(v.y, g.y, r.y);
-                        v.z = gate_residual2(v.z, g.z, r.z);
-                        v.w = gate_residual2(v.w, g.w, r.w);
-                    }
+                    const uint4 g = one_gate ? g_wave : *reinterpret_cast<const uint4*>(gate_row(a, m) + n);
+                    v.x = gate_residual2(v.x, g.x, res[it].x);
+                    v.y = gate_residual2(v.y, g.y, res[it].y);
+                    v.z = gate_residual2(v.z, g.z, res[it].z);
+                    v.w = gate_residual2(v.w, g.w, res[it].w);
                     store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
                 }
             }

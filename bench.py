@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--two-pass", action="store_true",
                    help="run the modulation producers as two launches (absmax, pack) instead of the single launch")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    p.add_argument("--no-standalone", action="store_true",
+                   help="skip the standalone cold/warm producer timings (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="before timing, copy 1 GiB once (a plain copy kernel of known size, for scaling "
                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -241,7 +243,7 @@ def main():
     med = {label: float(np.median(v)) for label, v in per.items()}
     launch_pct = {label: {"p50": round(float(np.percentile(v, 50)), 4), "p95": round(float(np.percentile(v, 95)), 4)}
                   for label, v in per.items()}
-    standalone = standalone_producers(seq, stream, dev, reps=20)
+    standalone = {} if args.no_standalone else standalone_producers(seq, stream, dev, reps=20)
 
     # algorithmic work
     def mod_bytes(K):  # two reads of x + QDATA + SFA written (padded rows included)

@@ -183,13 +183,17 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
  * accumulated in binary32 in an order of the kernel's choosing.
  * Requirements: K % 64 == 0, N % 16 == 0, ldo >= N, ldo % 4 == 0,
  * M_pad >= M, qa/qw 16-byte aligned, sfa/sfw 4-byte aligned, out 8-byte
- * aligned. */
+ * aligned; N * K/2 <= 2^32 (the packed weight within 4 GiB), K <= 2^25,
+ * M_pad < 2^31.  The activation may exceed 4 GiB: the rows are then computed
+ * in chunks of floor(2^32 / (K/2)) rounded down to a multiple of 256, one
+ * launch sequence per chunk in stream order. */
 nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
                         int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,
                         int64_t N, int64_t K, uint16_t* out, int64_t ldo, void* stream);
 
 /* Bytes of device workspace nvfp4_gemm_ws uses for an [M,K] x [N,K] product
- * (0 when it has nothing to split).  Depends on the shape only. */
+ * (0 when it has nothing to split; for an activation in several row chunks,
+ * the largest chunk's need).  Depends on the shape only. */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* nvfp4_gemm with a caller-owned workspace of at least

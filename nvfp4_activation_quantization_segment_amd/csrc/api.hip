@@ -212,14 +212,20 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
     return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
 }
 
+// Activation rows per launch: every byte offset into qa stays below 2^32
+// (the kernel's offsets are 32-bit), in whole 256-row tiles; 0 when K is too
+// wide for even one tile (K > 2^25).
+static int64_t gemm_chunk_rows(int64_t K) { return (((int64_t)1 << 32) / (K / 2)) / 256 * 256; }
+
 static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
                               int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N,
                               int64_t K, uint16_t* out, int64_t ldo, GemmArgs* a) {
     if (!qa || !sfa || !a_scale || !qw || !sfw || !w_scale || !out) return NVFP4_ERR_INVALID_ARGUMENT;
     if (M <= 0 || N <= 0 || K <= 0 || ldo < N || M_pad < M) return NVFP4_ERR_INVALID_ARGUMENT;
     if (K % 64 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
-    // 32-bit byte offsets inside the kernel
-    if (M_pad * (K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+    // 32-bit byte offsets inside the kernel: the weight must fit them; the
+    // activation is launched in row chunks that do (run_gemm)
+    if (N * (K / 2) > ((int64_t)1 << 32) || gemm_chunk_rows(K) == 0) return NVFP4_ERR_SHAPE;
     if (M_pad >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
     if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sfa, 4) || !aligned(sfw, 4) || !aligned(out, 8) ||
         ldo % 4 != 0 || !aligned(a_scale, 4) || !aligned(w_scale, 4))
@@ -246,20 +252,55 @@ static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float
     return NVFP4_OK;
 }
 
+// Workspace of the largest row chunk's plan (the chunks run in stream order
+// and share it).
+static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
+    const int64_t mc = gemm_chunk_rows(K);
+    if (M <= mc) return gemm_plan(M, N, K).workspace_bytes;
+    const size_t full = gemm_plan(mc, N, K).workspace_bytes;
+    const int64_t last = M - (M - 1) / mc * mc;
+    const size_t tail = gemm_plan(last, N, K).workspace_bytes;
+    return full > tail ? full : tail;
+}
+
+// The GEMM as row chunks of gemm_chunk_rows(K): each launch sees its chunk's
+// rows of qa, sfa, out and the residual from row 0, and the gate segment
+// bounds shifted by the chunk's first row.
+static nvfp4_status run_gemm(const GemmArgs& a, int64_t M, int64_t M_pad, void* workspace, bool use_ws,
+                             hipStream_t s) {
+    const int64_t mc = gemm_chunk_rows(a.K);
+    for (int64_t r0 = 0; r0 < M; r0 += mc) {
+        GemmArgs c = a;
+        c.M = (int32_t)(M - r0 < mc ? M - r0 : mc);
+        c.M_pad = (int32_t)(M_pad - r0 < mc ? M_pad - r0 : mc);
+        c.qa = a.qa + r0 * (a.K / 2);
+        c.sfa = a.sfa + r0 * (a.K / 16);
+        c.out = a.out + r0 * a.ldo;
+        if (a.epi) {
+            c.residual = a.residual + r0 * a.ldr;
+            for (int i = 0; i <= a.nseg; ++i) c.row_start[i] = (int32_t)(a.row_start[i] - r0);
+        }
+        const bool split = use_ws && gemm_plan(c.M, c.N, c.K).workspace_bytes > 0;
+        const nvfp4_status st = hip_status(launch_gemm(c, split ? (float*)workspace : nullptr, split, s));
+        if (st != NVFP4_OK) return st;
+    }
+    return NVFP4_OK;
+}
+
 nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
                         const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N, int64_t K,
                         uint16_t* out, int64_t ldo, void* stream) {
     GemmArgs a;
     const nvfp4_status st = gemm_args(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, &a);
     if (st != NVFP4_OK) return st;
-    return hip_status(launch_gemm(a, nullptr, false, (hipStream_t)stream));
+    return run_gemm(a, M, M_pad, nullptr, false, (hipStream_t)stream);
 }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) ||
-        K >= ((int64_t)1 << 31))
+        K >= ((int64_t)1 << 31) || gemm_chunk_rows(K) == 0)
         return 0;
-    return gemm_plan(M, N, K).workspace_bytes;
+    return gemm_workspace(M, N, K);
 }
 
 nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M, int64_t M_pad,
@@ -268,12 +309,12 @@ nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a
     GemmArgs a;
     const nvfp4_status st = gemm_args(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, &a);
     if (st != NVFP4_OK) return st;
-    const size_t need = gemm_plan(M, N, K).workspace_bytes;
+    const size_t need = gemm_workspace(M, N, K);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return NVFP4_ERR_INVALID_ARGUMENT;
         if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGNMENT;
     }
-    return hip_status(launch_gemm(a, (float*)workspace, need > 0, (hipStream_t)stream));
+    return run_gemm(a, M, M_pad, workspace, need > 0, (hipStream_t)stream);
 }
 
 nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
@@ -292,7 +333,7 @@ nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, con
     if (gates->ld < N || ldr < N) return NVFP4_ERR_INVALID_ARGUMENT;
     if (gates->ld % 4 != 0 || ldr % 4 != 0 || !aligned(gates->gate, 8) || !aligned(residual, 8))
         return NVFP4_ERR_ALIGNMENT;
-    const size_t need = gemm_plan(M, N, K).workspace_bytes;
+    const size_t need = gemm_workspace(M, N, K);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return NVFP4_ERR_INVALID_ARGUMENT;
         if (!aligned(workspace, 16)) return NVFP4_ERR_ALIGNMENT;
@@ -304,7 +345,7 @@ nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, con
     a.ld_gate = gates->ld;
     a.residual = residual;
     a.ldr = ldr;
-    return hip_status(launch_gemm(a, (float*)workspace, need > 0, (hipStream_t)stream));
+    return run_gemm(a, M, M_pad, workspace, need > 0, (hipStream_t)stream);
 }
 
 static nvfp4_status step(int which, const void* a, const void* b, const void* c, void* out, int64_t n,

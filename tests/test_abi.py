@@ -62,6 +62,8 @@ def test_gemm_argument_errors(pkg):
     assert g(None, P, P, 10, 64, P, P, P, 64, 64, P, 64, None) == 1
     assert g(P, P, P, 0, 64, P, P, P, 64, 64, P, 64, None) == 1
     assert g(P, P, P, 10, 64, P, P, P, 64, 48, P, 64, None) == 2       # K % 64
+    assert g(P, P, P, 10, 64, P, P, P, 1 << 20, 1 << 14, P, 1 << 20, None) == 2   # weight past 4 GiB
+    assert g(P, P, P, 10, 64, P, P, P, 16, 1 << 26, P, 16, None) == 2  # K > 2^25
     assert g(P, P, P, 10, 64, P, P, P, 40, 64, P, 64, None) == 2       # N % 16
     assert g(P, P, P, 10, 8, P, P, P, 64, 64, P, 64, None) == 1        # M_pad < M
     assert g(P, P, P, 10, 64, P, P, P, 64, 64, P, 32, None) == 1       # ldo < N
@@ -79,6 +81,10 @@ def test_gemm_workspace_plan(pkg):
     assert wsb(37810, 21504, 5376) == 0      # 12432 tiles: tail of 144 > 256/3
     assert wsb(37810, 14336, 5376) == 0      # 8288 tiles: tail of 96 > 256/3
     assert wsb(37810, 5376, 14336) == 36 * 7 * tile
+    # an activation past 4 GiB runs in row chunks of 599,040 rows at K = 14336:
+    # the full chunk (2340 x 1 tiles: 36 tail tiles in 7 ranges) needs more
+    # than the last one (960 rows: 4 tiles in 14 ranges of 16 steps)
+    assert wsb(600_000, 256, 14336) == 36 * 7 * tile
     assert wsb(1, 16, 64) == 0               # one K step: nothing to split
     assert wsb(64, 16, 5376) == 11 * tile    # one tile, 84 steps in 11 ranges of 8
     assert wsb(10, 16, 48) == 0              # invalid K

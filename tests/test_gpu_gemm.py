@@ -422,3 +422,57 @@ def test_attention_output_projection_with_residual_epilogue(m):
     err = np.abs(got - ref)
     assert np.all(err <= bound), float(np.max(err / bound))
     del keep
+
+
+def test_activation_past_4_gib_runs_in_row_chunks(m):
+    """M = 600,000 rows at K = 14,336: the packed activation (4.30 GB) exceeds
+    the kernel's 32-bit offsets and runs as two row chunks (599,040 + 960
+    rows).  A repeats a seeded 61-row block (tiled on the device; the oracle
+    runs on the block).  nvfp4_gemm_ws with random weights against the FP64
+    oracle on rows sampled on both sides of the chunk boundary; the residual
+    epilogue with a partial identity weight (every output one product, so
+    bit-exact) and a gate segment boundary inside the second chunk."""
+    dev = device()
+    M, N, K, P = 600_000, 256, 14336, 61
+    m_pad = oracle.padded_rows(M)
+    assert m_pad * K // 2 > 1 << 32
+    a = synth.add_outliers_t3(synth.normal_bf16(50, 0, (P, K), 1.0), 50, 0.001, 20.0)
+    sa, qa, sfa, _ = _par.quantize_bf16(a, P)
+    reps = -(-m_pad // P)
+    qa_d = to_dev(qa).repeat(reps, 1)[:m_pad].contiguous()
+    sfa_d = to_dev(sfa).repeat(reps, 1)[:m_pad].contiguous()
+    sa_d = to_dev(np.array([sa], np.float32))
+    rows = np.unique(np.concatenate([
+        np.array([0, 1, 255, 256, 599_039, 599_040, 599_041, 599_099, 599_100, M - 2, M - 1]),
+        synth.sample_rows(51, M, 96)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    print(f"A [{m_pad}, {K // 2}] packed, {rows.size} checked rows", flush=True)
+
+    w = bf16_np(0.02 * np.random.default_rng(52).standard_normal((N, K)))
+    sw, qw, sfw, _ = _par.quantize_bf16(w)
+    need = m.nvfp4_gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    m.nvfp4_gemm_ws(qa_d, sfa_d, sa_d, M, m_pad, to_dev(qw), to_dev(sfw), to_dev(np.array([sw], np.float32)), N, K,
+                    out, N, ws, need)
+    torch.cuda.synchronize()
+    check(_par.gemm_rows(qa, sfa, sa, qw, sfw, sw, rows % P), out_f64(out[ridx]), "row chunks")
+    del out
+
+    eye = np.zeros((N, K), np.uint16)
+    eye[np.arange(N), np.arange(N)] = 0x3F80
+    sw, qw, sfw, _ = _par.quantize_bf16(eye)
+    rs = np.array([0, 599_100, M], np.int64)
+    gate = bf16_np(1 + 0.3 * np.random.default_rng(53).standard_normal((2, N)))
+    rblock = synth.normal_bf16(54, 0, (P, N), 1.0)
+    res = to_dev_u16(rblock).repeat(reps, 1)[:M].contiguous()
+    gates, keep = m.make_row_gates(rs, to_dev_u16(gate))
+    m.nvfp4_gemm_gate_residual(qa_d, sfa_d, sa_d, M, m_pad, to_dev(qw), to_dev(sfw),
+                               to_dev(np.array([sw], np.float32)), N, K, gates, res, N, res, N, ws, need)
+    torch.cuda.synchronize()
+    del keep
+    o = _par.gemm_bf16_rows(qa, sfa, sa, qw, sfw, sw, rows % P)
+    seg_rs = np.array([0, int(np.searchsorted(rows, 599_100)), rows.size], np.int64)
+    want = oracle.gate_residual_rows(o, seg_rs, gate, rblock[rows % P])
+    got = host_u16(res[ridx])
+    assert np.array_equal(got, want), first_mismatch(got, want)

@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--no-attn-out", action="store_true",
                    help="skip the separately timed attention-output projection")
     p.add_argument("--two-pass", action="store_true",
-                   help="run the modulation producers as two launches (absmax, pack) instead of the single launch")
+                   help="run every producer as its two passes (absmax, pack: separate calls, per-pass times) instead of one call")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
     p.add_argument("--no-standalone", action="store_true",
                    help="skip the standalone cold/warm producer timings (profiling runs)")
@@ -185,12 +185,17 @@ def main():
                             b["gws_bytes"], stream)))
         b = bufs["fc2"]
         qw, sfw, tw = weights["fc2"]
-        seq.append(("fc2.absmax", "swiglu_absmax",
-                    lambda: nv.nvfp4_swiglu_absmax(gate_ptr, up_ptr, M, F, 2 * F, b["ws"], b["ts"], b["amax"],
-                                                   stream)))
-        seq.append(("fc2.pack", "swiglu_pack",
-                    lambda: nv.nvfp4_swiglu_pack(gate_ptr, up_ptr, M, F, 2 * F, b["ts"], b["q"], b["s"], M_pad,
-                                                 stream)))
+        if args.two_pass:
+            seq.append(("fc2.absmax", "swiglu_absmax",
+                        lambda: nv.nvfp4_swiglu_absmax(gate_ptr, up_ptr, M, F, 2 * F, b["ws"], b["ts"], b["amax"],
+                                                       stream)))
+            seq.append(("fc2.pack", "swiglu_pack",
+                        lambda: nv.nvfp4_swiglu_pack(gate_ptr, up_ptr, M, F, 2 * F, b["ts"], b["q"], b["s"], M_pad,
+                                                     stream)))
+        else:
+            seq.append(("fc2.quantize", "swiglu_quantize",
+                        lambda: nv.nvfp4_swiglu_quantize(gate_ptr, up_ptr, M, F, 2 * F, b["ws"], b["ts"], b["amax"],
+                                                         b["q"], b["s"], M_pad, stream)))
         seq.append(("fc2.gemm", "gemm",
                     lambda: nv.nvfp4_gemm_ws(b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, wf2.N, wf2.K, b["out"],
                                              wf2.N, b["gws"], b["gws_bytes"], stream)))

@@ -172,6 +172,14 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
                                int64_t ld, const float* tensor_scale, uint8_t* qdata, uint8_t* sfa,
                                int64_t M_pad, void* stream);
 
+/* Both SwiGLU passes in one call (same results as nvfp4_swiglu_absmax
+ * followed by nvfp4_swiglu_pack): the silu table is filled once for the two
+ * passes.  Same arguments, requirements and errors as the two calls
+ * together. */
+nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F,
+                                   int64_t ld, void* workspace, float* tensor_scale, float* amax_out,
+                                   uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);
+
 /* Block-scaled GEMM ("FC2 NVFP4 Library Scheduling", Exact Operation;
  * "NVFP4 Streaming Design", P0: FP32 global-scale product applied before the
  * BF16 conversion):

@@ -61,6 +61,7 @@ def _load():
         "nvfp4_quantize": (I32, [P, I64, I64, I64, P, P, P, P, P, I64, V]),
         "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
         "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
+        "nvfp4_swiglu_quantize": (I32, [P, P, I64, I64, I64, P, P, P, P, P, I64, V]),
         "nvfp4_gemm": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, V]),
         "nvfp4_gemm_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64]),
         "nvfp4_gemm_ws": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, P, ctypes.c_size_t, V]),
@@ -184,6 +185,12 @@ def nvfp4_swiglu_pack(gate, up, M, F, ld, tensor_scale, qdata, sfa, M_pad, strea
                                  _stream(stream)))
 
 
+def nvfp4_swiglu_quantize(gate, up, M, F, ld, workspace, tensor_scale, amax, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_swiglu_quantize",
+           lib.nvfp4_swiglu_quantize(_ptr(gate), _ptr(up), M, F, ld, _ptr(workspace), _ptr(tensor_scale), _ptr(amax),
+                                     _ptr(qdata), _ptr(sfa), M_pad, _stream(stream)))
+
+
 def nvfp4_gemm(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, ldo, stream=None):
     _check("nvfp4_gemm",
            lib.nvfp4_gemm(_ptr(qa), _ptr(sfa), _ptr(a_scale), M, M_pad, _ptr(qw), _ptr(sfw), _ptr(w_scale), N, K,
@@ -274,8 +281,11 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
     return q, s, ts, amax
 
 
-def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None):
-    """gate/up [M, 2F] bf16 (gate = first F columns) -> (qdata, sfa, tensor_scale, amax)."""
+def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, combined: bool = True):
+    """gate/up [M, 2F] bf16 (gate = first F columns) -> (qdata, sfa, tensor_scale, amax).
+
+    combined: one nvfp4_swiglu_quantize call; else nvfp4_swiglu_absmax then
+    nvfp4_swiglu_pack (identical bytes)."""
     _bits16(gu)
     M, F2 = gu.shape
     F = F2 // 2
@@ -288,8 +298,11 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None):
     q = torch.empty((m_pad, F // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
     up = gu.data_ptr() + F * gu.element_size()
-    nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, stream)
-    nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, stream)
+    if combined:
+        nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, q, s, m_pad, stream)
+    else:
+        nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, stream)
+        nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, stream)
     return q, s, ts, amax
 
 

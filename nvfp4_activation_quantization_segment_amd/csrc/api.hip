@@ -195,7 +195,7 @@ nvfp4_status nvfp4_swiglu_absmax(const uint16_t* gate, const uint16_t* up, int64
     if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
     const RowGeo g = row_geo(M, M, F, ld, kAbsmaxWgs, 0, 8);
-    return hip_status(launch_swiglu_absmax(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out,
+    return hip_status(launch_swiglu_absmax(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out, true,
                                            (hipStream_t)stream));
 }
 
@@ -209,7 +209,25 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
     if (!aligned(tensor_scale, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     const RowGeo g = row_geo(M, M_pad, F, ld, kSwigluPackWgs, 1, 16);
-    return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, (hipStream_t)stream));
+    return hip_status(launch_swiglu_pack(gate, up, g, tensor_scale, qdata, sfa, true, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F, int64_t ld,
+                                   void* workspace, float* tensor_scale, float* amax_out, uint8_t* qdata,
+                                   uint8_t* sfa, int64_t M_pad, void* stream) {
+    nvfp4_status st = check_rows(gate, M, F, ld);
+    if (st != NVFP4_OK) return st;
+    if ((st = check_rows(up, M, F, ld)) != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const RowGeo g1 = row_geo(M, M, F, ld, kAbsmaxWgs, 0, 8);
+    if ((st = hip_status(launch_swiglu_absmax(gate, up, g1, (uint32_t*)workspace, tensor_scale, amax_out, true, s))) !=
+        NVFP4_OK)
+        return st;
+    const RowGeo g2 = row_geo(M, M_pad, F, ld, kSwigluPackWgs, 1, 16);
+    return hip_status(launch_swiglu_pack(gate, up, g2, tensor_scale, qdata, sfa, false, s));
 }
 
 // Activation rows per launch: every byte offset into qa stays below 2^32

@@ -50,10 +50,11 @@ int modulate_quantize_grid();
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
                                     float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
                                     hipStream_t s);
+// fill: enqueue the silu table fill first (each public entry point does once)
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
-                                float* tensor_scale, float* amax_out, hipStream_t s);
+                                float* tensor_scale, float* amax_out, bool fill, hipStream_t s);
 hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,
-                              uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+                              uint8_t* qdata, uint8_t* sfa, bool fill, hipStream_t s);
 hipError_t launch_step(int which, const void* a, const void* b, const void* c, void* out, int64_t n, hipStream_t s);
 
 struct GemmArgs {

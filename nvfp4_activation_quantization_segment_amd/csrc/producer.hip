@@ -1137,16 +1137,16 @@ static void launch_silu_fill(hipStream_t s) {
 }
 
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
-                                float* tensor_scale, float* amax_out, hipStream_t s) {
-    launch_silu_fill(s);
+                                float* tensor_scale, float* amax_out, bool fill, hipStream_t s) {
+    if (fill) launch_silu_fill(s);
     hipLaunchKernelGGL(swiglu_absmax_kernel, dim3(g.grid), dim3(g.block), 0, s, gate, up, g, ws, tensor_scale,
                        amax_out);
     return hipGetLastError();
 }
 
 hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,
-                              uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
-    launch_silu_fill(s);
+                              uint8_t* qdata, uint8_t* sfa, bool fill, hipStream_t s) {
+    if (fill) launch_silu_fill(s);
     const bool off32 = ((g.M - 1) * g.ldx + 8 * (int64_t)g.C8) * 2 < ((int64_t)1 << 32) &&
                        g.rows_total * 4 * (int64_t)g.C8 < ((int64_t)1 << 32);
     if (off32)

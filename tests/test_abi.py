@@ -133,6 +133,12 @@ def test_producer_argument_errors(pkg):
     assert L.nvfp4_quantize(FAKE, 10, 64, 64, ws, ts, None, q + 2, s, 64, None) == 3       # qdata
     assert L.nvfp4_swiglu_absmax(FAKE, FAKE, 10, 24, 48, ws, ts, None, None) == 2
     assert L.nvfp4_swiglu_pack(FAKE, None, 10, 32, 64, ts, q, s, 64, None) == 1
+    sq = L.nvfp4_swiglu_quantize
+    assert sq(FAKE, None, 10, 32, 64, ws, ts, None, q, s, 64, None) == 1                  # up
+    assert sq(FAKE, FAKE, 10, 24, 48, ws, ts, None, q, s, 64, None) == 2                  # F % 16
+    assert sq(FAKE, FAKE, 10, 32, 64, None, ts, None, q, s, 64, None) == 1                # workspace
+    assert sq(FAKE, FAKE, 10, 32, 64, ws, ts, None, q, s, 32, None) == 2                  # M_pad
+    assert sq(FAKE, FAKE, 10, 32, 64, ws, ts, None, q + 1, s, 64, None) == 3              # qdata
 
 
 def test_gate_residual_argument_errors(pkg):

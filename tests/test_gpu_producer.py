@@ -299,14 +299,17 @@ def check_swiglu(m, gu, m_pad=None):
     M = gu.shape[0]
     m_pad = oracle.padded_rows(M) if m_pad is None else m_pad
     s_g, q, s, amax = _par.swiglu_quantize(gu, m_pad)
-    gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu), m_pad=m_pad)
-    torch.cuda.synchronize()
-    assert host(gamax)[0] == amax and host(gts)[0] == s_g
-    assert np.array_equal(host(gs), s), first_mismatch(host(gs), s)
-    assert np.array_equal(host(gq), q), first_mismatch(host(gq), q)
+    for combined in (True, False):
+        gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu), m_pad=m_pad, combined=combined)
+        torch.cuda.synchronize()
+        path = "one call" if combined else "two calls"
+        assert host(gamax)[0] == amax and host(gts)[0] == s_g, path
+        assert np.array_equal(host(gs), s), path + ": SFA " + str(first_mismatch(host(gs), s))
+        assert np.array_equal(host(gq), q), path + ": QDATA " + str(first_mismatch(host(gq), q))
 
 
-@pytest.mark.parametrize("M,F", [(1, 16), (77, 48), (200, 512), (65, 8208)])
+# F = 16400: more than 1024 blocks per row, so pack threads take two blocks
+@pytest.mark.parametrize("M,F", [(1, 16), (77, 48), (200, 512), (65, 8208), (5, 16400)])
 def test_swiglu_small_shapes(m, M, F):
     rng = np.random.default_rng(M + F)
     gu = bf16_np(3 * rng.standard_normal((M, 2 * F)))

@@ -173,9 +173,13 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
                                int64_t M_pad, void* stream);
 
 /* Both SwiGLU passes in one call (same results as nvfp4_swiglu_absmax
- * followed by nvfp4_swiglu_pack): the silu table is filled once for the two
- * passes.  Same arguments, requirements and errors as the two calls
- * together. */
+ * followed by nvfp4_swiglu_pack, byte for byte): after the silu table fill,
+ * one launch runs pass 1, a grid barrier and pass 2, keeping h of the rows
+ * each workgroup visited last in registers, as nvfp4_modulate_quantize does
+ * (same workspace, same barrier and the same failure mode when other streams
+ * keep compute units occupied past 1 s).  When F > 16384, or gate/up spans
+ * 4 GiB or more, it enqueues the two passes instead.  Same arguments,
+ * requirements and errors as the two calls together. */
 nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F,
                                    int64_t ld, void* workspace, float* tensor_scale, float* amax_out,
                                    uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);

@@ -222,6 +222,15 @@ nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int
     if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
+    // one launch when a row fits one workgroup and every byte offset into
+    // gate, up, qdata and sfa fits 32 bits
+    const bool off32 = ((M - 1) * ld + F) * 2 < ((int64_t)1 << 32) && M_pad * (F / 2) < ((int64_t)1 << 32);
+    const int G = (F / 16 <= 1024 && off32) ? swiglu_quantize_grid() : 0;
+    if (G > 0) {
+        const RowGeo g = row_geo(M, M_pad, F, ld, G, 1, 16);
+        return hip_status(
+            launch_swiglu_quantize(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out, qdata, sfa, s));
+    }
     const RowGeo g1 = row_geo(M, M, F, ld, kAbsmaxWgs, 0, 8);
     if ((st = hip_status(launch_swiglu_absmax(gate, up, g1, (uint32_t*)workspace, tensor_scale, amax_out, true, s))) !=
         NVFP4_OK)

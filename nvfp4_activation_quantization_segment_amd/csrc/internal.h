@@ -50,6 +50,11 @@ int modulate_quantize_grid();
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
                                     float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
                                     hipStream_t s);
+// Both SwiGLU passes in one launch (after the silu table fill); the grid of
+// swiglu_quantize_grid() keeps every workgroup resident.
+int swiglu_quantize_grid();
+hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
+                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, hipStream_t s);
 // fill: enqueue the silu table fill first (each public entry point does once)
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, bool fill, hipStream_t s);

@@ -995,6 +995,132 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
+// Single-launch SwiGLU producer
+//
+// The structure of the modulation single launch with the SwiGLU input: h of
+// the row groups a workgroup visits last stays in registers across the grid
+// barrier (the silu table fills the LDS, so none is held there); pass 2 packs
+// those first and reads gate and up again for the rest, last to first.  The
+// silu table is filled by silu_lut_fill_kernel before the launch.
+// ---------------------------------------------------------------------------
+constexpr int kSwigluHoldRegs = 8;  // row groups held in registers per thread
+
+// h of 16 columns as packed bf16 words (the pass-1 form, also what is held).
+__device__ __forceinline__ void swiglu16_pk(const uint16_t* lut, const uint4& g0, const uint4& g1, const uint4& u0,
+                                            const uint4& u1, uint32_t h[8]) {
+    swiglu8(lut, g0, u0, h);
+    swiglu8(lut, g1, u1, h + 4);
+}
+
+__global__ __launch_bounds__(1024) void swiglu_quantize_kernel(const uint16_t* __restrict__ gate,
+                                                               const uint16_t* __restrict__ up, RowGeo g,
+                                                               uint32_t* ws, float* tensor_scale, float* amax_out,
+                                                               uint8_t* __restrict__ qdata,
+                                                               uint8_t* __restrict__ sfa) {
+    __shared__ __attribute__((aligned(16))) uint16_t slut[65536];
+    __shared__ float2 dr[128];
+    const uint64_t gen = grid_generation(ws);
+    lut_to_lds(slut);
+    const char* gb = reinterpret_cast<const char*>(gate);
+    const char* ub = reinterpret_cast<const char*>(up);
+    const int C16 = g.C8 >> 1;
+    const int rho = threadIdx.x / C16, b = threadIdx.x - rho * C16;
+    const bool on = rho < g.R;
+    const int64_t groups = (g.M + g.R - 1) / g.R;
+    constexpr int HR = kSwigluHoldRegs;
+    const HoldSplit hs = hold_split(groups, 0, HR);
+    const int gstride = (int)gridDim.x * g.R;
+    const int r_first = (int)blockIdx.x * g.R + rho;  // row of local group 0
+    const uint32_t xrow = 2u * (uint32_t)g.ldx, xcol = 32u * (uint32_t)b;
+
+    // ---- pass 1: every streamed group for its maximum, then the held ones ----
+    uint32_t m2 = 0;
+    uint32_t hy[HR][8];
+    if (on) {
+        for (int t = 0; t < hs.ns; ++t) {
+            const uint32_t o = (uint32_t)(r_first + t * gstride) * xrow + xcol;
+            uint32_t h[8];
+            swiglu16_pk(slut, ld16o(gb, o), ld16o(gb, o + 16), ld16o(ub, o), ld16o(ub, o + 16), h);
+            max16(m2, h);
+        }
+#pragma unroll
+        for (int k = 0; k < HR; ++k) {
+            const int r = r_first + (hs.ns + k) * gstride;
+            if (k < hs.nr && r < g.M) {
+                const uint32_t o = (uint32_t)r * xrow + xcol;
+                swiglu16_pk(slut, ld16o(gb, o), ld16o(gb, o + 16), ld16o(ub, o), ld16o(ub, o + 16), hy[k]);
+                max16(m2, hy[k]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) hy[k][j] = 0u;
+            }
+        }
+    }
+    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, gen, tensor_scale, amax_out);
+
+    // ---- pass 2 ----
+    const float amax = __uint_as_float(bits << 16);
+    const float s_g = (amax == 0.0f) ? 1.0f : amax / 2688.0f;
+    build_dr_table(dr, s_g);
+    const bool sg_fast = scale_in_fast_range(s_g);
+    const float rg = 1.0f / s_g;
+    zero_pad_rows(g, qdata, sfa);
+    const uint32_t qrow = 8u * (uint32_t)C16, srow = (uint32_t)C16;
+    const uint32_t qcol = 8u * (uint32_t)b;
+    if (on) {
+#pragma unroll
+        for (int k = 0; k < HR; ++k) {
+            const int r = r_first + (hs.ns + k) * gstride;
+            if (k < hs.nr && r < g.M)
+                pack_block16_store(hy[k], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
+                                   b);
+        }
+    }
+    auto put = [&](const PackedBlock& pb, int r) {
+        store_block(pb, qdata + ((uint32_t)r * qrow + qcol), sfa + ((uint32_t)r * srow + b));
+    };
+    auto pack = [&](const uint4& g0, const uint4& g1, const uint4& u0, const uint4& u1) {
+        float h[16];
+        const float m = swiglu16_f32(slut, g0, g1, u0, u1, h);
+        return pack16f(h, m, s_g, rg, sg_fast, dr);
+    };
+    // Streamed groups last to first, two per iteration, as in the modulation
+    // single launch: the next pair's loads ahead of this pair's stores, and a
+    // bare s_barrier keeping the waves in step.
+    int t = hs.ns - 1;
+    if (t < 0) return;  // uniform over the workgroup
+    uint4 ga0, ga1, ua0, ua1, gb0, gb1, ub0, ub1;
+    auto load_pair = [&](int tt) {
+        const uint32_t o0 = (uint32_t)(r_first + tt * gstride) * xrow + xcol;
+        const uint32_t o1 = o0 - (uint32_t)gstride * xrow;
+        ga0 = ld16o(gb, o0);
+        ga1 = ld16o(gb, o0 + 16);
+        ua0 = ld16o(ub, o0);
+        ua1 = ld16o(ub, o0 + 16);
+        gb0 = ld16o(gb, o1);
+        gb1 = ld16o(gb, o1 + 16);
+        ub0 = ld16o(ub, o1);
+        ub1 = ld16o(ub, o1 + 16);
+    };
+    if (t >= 1 && on) load_pair(t);
+    for (; t >= 1; t -= 2) {
+        if (on) {
+            const int r0 = r_first + t * gstride, r1 = r0 - gstride;
+            const PackedBlock p0 = pack(ga0, ga1, ua0, ua1);
+            const PackedBlock p1 = pack(gb0, gb1, ub0, ub1);
+            if (t >= 3) load_pair(t - 2);
+            put(p0, r0);
+            put(p1, r1);
+        }
+        __builtin_amdgcn_s_barrier();
+    }
+    if (t == 0 && on) {
+        const uint32_t o0 = (uint32_t)r_first * xrow + xcol;
+        put(pack(ld16o(gb, o0), ld16o(gb, o0 + 16), ld16o(ub, o0), ld16o(ub, o0 + 16)), r_first);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Single-step kernels (elementwise, grid-stride)
 // ---------------------------------------------------------------------------
 __global__ void step_modulate_kernel(const uint16_t* x, const uint16_t* sc, const uint16_t* sh, uint16_t* y,
@@ -1115,6 +1241,24 @@ int modulate_quantize_grid() {
     return resident_grid((const void*)modulate_quantize_kernel<false>, cache);
 }
 
+static void launch_silu_fill(hipStream_t s) {
+    hipLaunchKernelGGL(silu_lut_fill_kernel, dim3(256), dim3(256), 0, s);
+}
+
+int swiglu_quantize_grid() {
+    static int cache[kMaxDevices] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1,
+                                     -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+    return resident_grid((const void*)swiglu_quantize_kernel, cache);
+}
+
+hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
+                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
+    launch_silu_fill(s);
+    hipLaunchKernelGGL(swiglu_quantize_kernel, dim3(g.grid), dim3(g.block), 0, s, gate, up, g, ws, tensor_scale,
+                       amax_out, qdata, sfa);
+    return hipGetLastError();
+}
+
 // A plain launch: the grid never exceeds what the device holds at once, so on
 // a device not kept busy by other streams every workgroup is resident and the
 // barrier completes (its wait is bounded in any case).  The cooperative launch
@@ -1132,9 +1276,6 @@ hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const Se
     return hipGetLastError();
 }
 
-static void launch_silu_fill(hipStream_t s) {
-    hipLaunchKernelGGL(silu_lut_fill_kernel, dim3(256), dim3(256), 0, s);
-}
 
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, bool fill, hipStream_t s) {

@@ -1003,7 +1003,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
 // those first and reads gate and up again for the rest, last to first.  The
 // silu table is filled by silu_lut_fill_kernel before the launch.
 // ---------------------------------------------------------------------------
-constexpr int kSwigluHoldRegs = 8;  // row groups held in registers per thread
+constexpr int kSwigluHoldRegs = 11;  // row groups held in registers per thread (123 VGPRs, no spills)
 
 // h of 16 columns as packed bf16 words (the pass-1 form, also what is held).
 __device__ __forceinline__ void swiglu16_pk(const uint16_t* lut, const uint4& g0, const uint4& g1, const uint4& u0,

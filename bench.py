@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--two-pass", action="store_true",
                    help="run every producer as its two passes (absmax, pack: separate calls, per-pass times) instead of one call")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    p.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the step's outputs")
     p.add_argument("--no-standalone", action="store_true",
                    help="skip the standalone cold/warm producer timings (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -248,6 +249,7 @@ def main():
     med = {label: float(np.median(v)) for label, v in per.items()}
     launch_pct = {label: {"p50": round(float(np.percentile(v, 50)), 4), "p95": round(float(np.percentile(v, 95)), 4)}
                   for label, v in per.items()}
+    hashes = {} if args.no_hash else output_hashes(bufs)
     standalone = {} if args.no_standalone else standalone_producers(seq, stream, dev, reps=20)
 
     # algorithmic work
@@ -321,6 +323,7 @@ def main():
         "timing": {"wall_ms_timed_region": round(wall_ms, 2), "event_ms_timed_region": round(total_ms, 2),
                    "setup_s": round(setup_s, 1), "kernel_source_hash": gemm_hash,
                    "launch_ms_in_step": launch_pct},
+        "output_sha256": hashes,
         "producer_standalone": {
             nme: dict(v, bytes=prod_bytes[nme],
                       frac_hbm_cold_p50=round(prod_bytes[nme] / (v["cold_p50_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
@@ -336,6 +339,27 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, x_h, segs, gu_h, (wq, wf1, wf2))
     print(json.dumps(result), flush=True)
+
+
+def output_hashes(bufs):
+    """SHA-256 of each projection's outputs after the timed steps: tensor scale
+    (its 4 bytes), QDATA and SFA (padding rows included) and the bf16 GEMM
+    output.  Every kernel sums in a fixed order, so these are the same on every
+    run and every device."""
+    import hashlib
+
+    import torch
+
+    def sha(t):
+        flat = t.contiguous().view(torch.uint8).view(-1)
+        h = hashlib.sha256()
+        step = 1 << 28
+        for i in range(0, flat.numel(), step):
+            h.update(flat[i:i + step].cpu().numpy().tobytes())
+        return h.hexdigest()
+
+    torch.cuda.synchronize()
+    return {name: {k: sha(b[k]) for k in ("ts", "q", "s", "out")} for name, b in bufs.items()}
 
 
 def standalone_producers(seq, stream, dev, reps):

@@ -1,6 +1,6 @@
 #!/usr/bin/env python3
-"""Benchmark: one step = the three NVFP4 projections of an H3 block at the
-canonical 37,810-token shape, each producer + GEMM on one stream:
+"""Benchmark: one step = the three NVFP4 projections of an H3 block at
+37,810 tokens, each producer + GEMM on one stream:
 
   QKV  modulation producer (x [37810,5376], 2 segments) -> GEMM N=21504, K=5376
   FC1  modulation producer (same x, own shift/scale)    -> GEMM N=14336, K=5376

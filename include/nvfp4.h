@@ -9,12 +9,12 @@
  *    rounding after each operation, reduces |y| to its absolute maximum in the
  *    first pass, and writes packed QDATA and E4M3 block scales into
  *    caller-owned buffers in the second; y never reaches memory.
- *  - "NVFP4 Streaming Design", Numerical Constraint: one exact global BF16
- *    absolute maximum, one FP32 tensor scale derived from it, one E4M3 block
- *    scale per 16 values, E2M1 values quantized with both scales; no tile can
+ *  - "NVFP4 Streaming Design", Numerical Constraint: the tensor's exact BF16
+ *    maximum magnitude gives a single FP32 tensor scale; each 16 values get
+ *    an E4M3 scale; E2M1 codes come from both scales; no tile can
  *    be packed before the global reduction completes (two passes).
- *  - "FC2 NVFP4 Library Scheduling", Exact Operation: row-major packed
- *    activation [M,K] times packed weight [N,K] to BF16 [M,N]; FP32 compute;
+ *  - "FC2 NVFP4 Library Scheduling", Exact Operation: packed activation rows
+ *    [M,K] against packed weight rows [N,K], giving BF16 [M,N]; FP32 compute;
  *    alpha = activation tensor scale * weight tensor scale, read from device
  *    memory; no bias; 37,810 logical rows padded to 37,824; the FC2 producer
  *    fuses an exact BF16 SwiGLU.
@@ -73,7 +73,7 @@ typedef enum {
 } nvfp4_status;
 
 /* Per-segment modulation parameters ("NVFP4 Modulation Producer Fusion",
- * Exactness Contract: segment-specific shift and scale selection).  Segment s
+ * Exactness Contract: each segment selects its own shift and scale).  Segment s
  * covers rows [row_start[s], row_start[s+1]); row_start has count+1 HOST
  * entries with row_start[0] = 0, strictly increasing, row_start[count] = M,
  * 1 <= count <= NVFP4_MAX_SEGMENTS.  shift and scale are DEVICE bf16 arrays
@@ -236,8 +236,8 @@ typedef struct {
 } nvfp4_row_gates;
 
 /* nvfp4_gemm_ws followed by the exact residual epilogue ("NVFP4 Streaming
- * Design", P4: the BF16 conversion, gate multiply, residual add and final BF16
- * rounding), fused into the GEMM's store:
+ * Design", P4: the GEMM result rounded to BF16, scaled by the gate, added to
+ * the residual and rounded to BF16 again), fused into the GEMM's store:
  *   o   = bf16(RN(alpha * sum_k A[m][k] * W[n][k]))   (the nvfp4_gemm output)
  *   out = bf16(RN(residual[m][n] + bf16(RN(gate[s][n] * o))))
  * with s the segment of row m; residual is bf16 [M, ldr].  out may be the

@@ -1,9 +1,9 @@
 // NVFP4 block-scaled GEMM for gfx950:  out = bf16(alpha * A W^T).
 //
-// Operation ("FC2 NVFP4 Library Scheduling", Exact Operation): row-major packed
-// activation [M,K] times packed weight [N,K] -> BF16 [M,N], FP32 accumulation,
-// alpha = activation tensor scale * weight tensor scale applied before the
-// BF16 conversion ("NVFP4 Streaming Design", P0).
+// Operation ("FC2 NVFP4 Library Scheduling", Exact Operation): packed
+// activation rows [M,K] against packed weight rows [N,K], giving BF16 [M,N],
+// FP32 accumulation, alpha = activation tensor scale * weight tensor scale
+// applied before the BF16 conversion ("NVFP4 Streaming Design", P0).
 //
 // Decode.  Every E2M1 value times an E4M3 scale has at most 6 significant bits
 // and lies in [2^-10, 2688], so it is exact in fp16; products of two such fp16
@@ -205,10 +205,10 @@ __device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_
     tn = (logical % gsz) / gm;
 }
 
-// Residual epilogue ("NVFP4 Streaming Design", P4: the BF16 conversion, gate
-// multiply, residual add and final BF16 rounding): for two packed outputs o2,
-// gates g2 and residuals r2, bf16(r + bf16(g * o)); the product of two bf16
-// values is exact in binary32.
+// Residual epilogue ("NVFP4 Streaming Design", P4: the GEMM result rounded to
+// BF16, scaled by the gate, added to the residual, rounded again): for two
+// packed outputs o2, gates g2 and residuals r2, bf16(r + bf16(g * o)); the
+// product of two bf16 values is exact in binary32.
 __device__ __forceinline__ uint32_t gate_residual2(uint32_t o2, uint32_t g2, uint32_t r2) {
     const float pa = round_bf16(bf16_lo(g2) * bf16_lo(o2)), pb = round_bf16(bf16_hi(g2) * bf16_hi(o2));
     return pack_bf16x2(bf16_lo(r2) + pa, bf16_hi(r2) + pb);

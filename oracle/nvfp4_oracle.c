@@ -164,7 +164,7 @@ float ora_tensor_scale(float amax) {
     return amax / 2688.0f;
 }
 
-/* One E4M3 block scale per 16 values: E4M3(RN(RN(a16 / 6) / s_g)). */
+/* The E4M3 scale of a 16-value block: E4M3(RN(RN(a16 / 6) / s_g)). */
 uint8_t ora_block_scale(float a16, float s_g) {
     float t6 = a16 / 6.0f;
     float t = t6 / s_g;
@@ -340,8 +340,8 @@ void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* Exact residual epilogue ("NVFP4 Streaming Design", P4: the BF16           */
-/* conversion, gate multiply, residual add and final BF16 rounding)          */
+/* Exact residual epilogue ("NVFP4 Streaming Design", P4): the GEMM result  */
+/* rounded to BF16, times the gate, plus the residual, rounded again         */
 /* ------------------------------------------------------------------------ */
 uint16_t ora_gate_residual(uint16_t o, uint16_t gate, uint16_t residual) {
     float g = ora_bf16_to_f32(gate) * ora_bf16_to_f32(o);

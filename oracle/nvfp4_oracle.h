@@ -14,12 +14,12 @@
  * Sources (page title, section):
  *  - "NVFP4 Modulation Producer Fusion", Exactness Contract: per-segment
  *    shift/scale selection, the (x*(scale+1))+shift order with BF16 rounding.
- *  - "NVFP4 Streaming Design", Numerical Constraint: one exact global BF16
- *    absolute maximum, one FP32 tensor scale derived from it, one E4M3 block
- *    scale per 16 values, E2M1 values quantized with both scales; no tile can
+ *  - "NVFP4 Streaming Design", Numerical Constraint: the tensor's exact BF16
+ *    maximum magnitude gives a single FP32 tensor scale; each 16 values get
+ *    an E4M3 scale; E2M1 codes come from both scales; no tile can
  *    be packed before the global reduction completes.
- *  - "FC2 NVFP4 Library Scheduling", Exact Operation: row-major packed
- *    activation [M,K] times packed weight [N,K] to BF16 [M,N], FP32 compute,
+ *  - "FC2 NVFP4 Library Scheduling", Exact Operation: packed activation rows
+ *    [M,K] against packed weight rows [N,K], giving BF16 [M,N], FP32 compute,
  *    alpha = activation tensor scale * weight tensor scale, 37,810 rows padded
  *    to 37,824; exact BF16 SwiGLU feeding the FC2 producer.
  *
@@ -92,8 +92,8 @@ void ora_e2m1_encode_batch(const float* v, int64_t n, uint8_t* code);
 void ora_e4m3_encode_batch(const float* t, int64_t n, uint8_t* code);
 
 /* ---- exact residual epilogue ("NVFP4 Streaming Design", P4) -------------- *
- * After the BF16 conversion of the GEMM output o: gate multiply, residual add
- * and final BF16 rounding, each a binary32 operation rounded to bf16:
+ * The GEMM's BF16 output o is scaled by the gate and added to the residual,
+ * each step one binary32 operation rounded to BF16:
  *   out = bf16(residual + bf16(gate * o))                                   */
 uint16_t ora_gate_residual(uint16_t o, uint16_t gate, uint16_t residual);
 /* The same over o [M, N] (row stride ldo): gate is [nseg, N] bf16 (row stride

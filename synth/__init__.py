@@ -5,7 +5,7 @@ generator) and knows the shapes of the workloads; it holds none of the
 quantizer's arithmetic.  It is the one module that both the oracle-side tests
 and the HIP-side tests and benchmark draw inputs from.
 
-Workloads (shapes of the pages' H3 block at the canonical 37,810-token shape;
+Workloads (shapes of the pages' H3 block at 37,810 tokens;
 synthetic data stands in for the captured activations, which are absent):
 
 =========  =====================================================================

@@ -543,10 +543,10 @@ __device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, uint64_t gen, f
             for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
             const uint64_t want = tagged(tag, late ? kAbandoned : (kPublished | mm));
             const uint64_t r = settle(&q[kResultQword], tag, want);
-            if (r == want) {
-                write_scale(outcome_bits(r), tensor_scale, amax_out);
-                if (!late) store_dev64(&q[kGenQword], tag);
-            }
+            // the outcome that holds, also when an abandon got there first
+            // (then every writer writes the same NaN)
+            write_scale(outcome_bits(r), tensor_scale, amax_out);
+            if (r == want && !late) store_dev64(&q[kGenQword], tag);
             result = outcome_bits(r);
         }
     } else if (threadIdx.x == 0) {

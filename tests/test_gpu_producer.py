@@ -182,6 +182,62 @@ def test_workspace_reuse_between_calls(m):
             assert int(w[64:72].view(np.uint64)[0]) == gen
 
 
+def test_abandoned_barrier_is_sticky_until_the_workspace_is_zeroed(m):
+    """The failure path of the single launches' grid barrier, forced from the
+    host without any wait: the workspace's result word is preset to an
+    abandoned barrier of the next generation (what a wait past its bound
+    leaves behind).  Every single-launch call on that workspace, modulation
+    and SwiGLU, then completes with a NaN tensor scale and amax, scale code
+    0x7F in every block and zero codes (padding rows zero), and leaves the
+    generation where it was; after a zero fill the next call is exact again.
+    White-box: the test writes the generation word (bytes 64..71) and the
+    result word (bytes 128..135) as (tag << 20) | 0x20000."""
+    dev = device()
+    rng = np.random.default_rng(7)
+    M, D = 130, 256
+    x = bf16_np(3 * rng.standard_normal((M, D)))
+    rs = [0, 100, M]
+    sh = bf16_np(0.1 * rng.standard_normal((2, D)))
+    sc = bf16_np(0.1 * rng.standard_normal((2, D)))
+    gu = bf16_np(2 * rng.standard_normal((M, 2 * D)))
+    ws = torch.zeros(int(m.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
+    gen = 5
+    words = ws.view(torch.int64)
+    words[8] = gen
+    words[16] = ((gen + 1) << 20) | 0x20000
+    m_pad = oracle.padded_rows(M)
+    seg, keep = m.make_segments(rs, to_dev_u16(sh), to_dev_u16(sc))
+    for kind in ("modulate", "swiglu", "modulate"):
+        ts = torch.zeros(1, dtype=torch.float32, device=dev)
+        a = torch.zeros(1, dtype=torch.float32, device=dev)
+        q = torch.full((m_pad, D // 2), 0x55, dtype=torch.uint8, device=dev)
+        s = torch.full((m_pad, D // 16), 0x55, dtype=torch.uint8, device=dev)
+        if kind == "modulate":
+            m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
+        else:
+            g = to_dev_u16(gu)
+            m.nvfp4_swiglu_quantize(g, g.data_ptr() + 2 * D, M, D, 2 * D, ws, ts, a, q, s, m_pad)
+        torch.cuda.synchronize()
+        assert np.isnan(host(ts)[0]) and np.isnan(host(a)[0]), kind
+        hs, hq = host(s), host(q)
+        assert (hs[:M] == 0x7F).all() and not hs[M:].any(), kind
+        assert not hq.any(), kind
+        assert int(host(words)[8]) == gen, kind
+    ws.zero_()
+    ts = torch.zeros(1, dtype=torch.float32, device=dev)
+    a = torch.zeros(1, dtype=torch.float32, device=dev)
+    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+    m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
+    torch.cuda.synchronize()
+    s_g, oq, os_, amax = _par.modulate_quantize(x, oracle.Segments(rs, sh, sc), m_pad)
+    assert host(ts)[0] == s_g and host(a)[0] == amax
+    assert np.array_equal(host(s), os_), first_mismatch(host(s), os_)
+    assert np.array_equal(host(q), oq), first_mismatch(host(q), oq)
+    assert int(host(words)[8]) == 1
+    del keep
+
+
 def test_non_default_stream(m):
     w = synth.workload("tiny")
     x = w.x()

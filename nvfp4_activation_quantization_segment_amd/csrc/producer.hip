@@ -887,6 +887,33 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     uint32_t m2 = 0;
     uint32_t hy[HR][8];
     int t = 0;
+    int s = 0, seg_hi = 0;
+    ColPk cp;
+    if (on) {
+        // LDS-held groups first, so that more of the rows read last (before
+        // the register-held ones) are rows pass 2 reads again, still in the
+        // memory-side cache when it starts (measured 0-2% faster)
+        for (int tl = hs.ns; tl < hs.ns + hs.nl; ++tl) {
+            const int r = r_first + tl * gstride;
+            const uint32_t o = (uint32_t)r * xrow + xcol;
+            const uint4 a = ld16o(xb, o), c = ld16o(xb, o + 16);
+            const uint32_t v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            uint32_t y[8];
+            if constexpr (PLAIN) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = v[k];
+            } else {
+                if (r >= seg_hi) {
+                    s = seg_find(seg, r, s);
+                    seg_hi = (int)seg.row_start[s + 1];
+                    load_cols_pk(seg, s, b, cp);
+                }
+                modulate16_pk(v, cp, y);
+            }
+            max16(m2, y);
+            hold_put(hold, tl - hs.ns, y);
+        }
+    }
     {
         // streamed groups, two per iteration, with binary32 column parameters
         // (short of VALU here, not of registers: the held groups come later)
@@ -924,31 +951,12 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                 absmax(b0, b1, r1);
             }
         }
+        if (t < hs.ns && on) {
+            const uint32_t o0 = (uint32_t)(r_first + t * gstride) * xrow + xcol;
+            absmax(ld16o(xb, o0), ld16o(xb, o0 + 16), r_first + t * gstride);
+        }
     }
     if (on) {
-        // held groups: packed column parameters, loaded at their first row
-        int s = 0, seg_hi = 0;
-        ColPk cp;
-        for (; t < hs.ns + hs.nl; ++t) {
-            const int r = r_first + t * gstride;
-            const uint32_t o = (uint32_t)r * xrow + xcol;
-            const uint4 a = ld16o(xb, o), c = ld16o(xb, o + 16);
-            const uint32_t v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-            uint32_t y[8];
-            if constexpr (PLAIN) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) y[k] = v[k];
-            } else {
-                if (r >= seg_hi) {
-                    s = seg_find(seg, r, s);
-                    seg_hi = (int)seg.row_start[s + 1];
-                    load_cols_pk(seg, s, b, cp);
-                }
-                modulate16_pk(v, cp, y);
-            }
-            max16(m2, y);
-            if (t >= hs.ns) hold_put(hold, t - hs.ns, y);
-        }
         // register-held groups: all loads first, then y in place of x
         const int t0 = hs.ns + hs.nl;
 #pragma unroll

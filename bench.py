@@ -557,7 +557,8 @@ def cpu_baseline(args, x_h, segs, gu_h, works):
         "gemm_TFLOPs": round(flop / t_gemm / 1e12, 6),
         "host_cores_available": cores,
         "all_cores": {"value": round(flop_n / (tp_n + tg_n) / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-                      "kind": "oracle on a thread pool (producer rows, GEMM output columns)", "seconds": round(tp_n + tg_n, 2)},
+                      "kind": "oracle on a thread pool (producer rows, GEMM output columns)",
+                      "seconds": round(tp_n + tg_n, 2)},
     }
 
 

@@ -137,7 +137,10 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
  * so long that its wait passes 1 s, the call completes with a NaN tensor
  * scale and amax, scale code 0x7F and zero codes in every block, and so does
  * every later single-launch call on that workspace until it is zero-filled
- * again.  When D > 16384, or x spans 4 GiB or more, it enqueues the two
+ * again.  Where other streams may run kernels on the device at the same time,
+ * use the two-pass entry points, which need no co-residency; calls that can
+ * overlap in time must use different workspaces in any case.  When
+ * D > 16384, or x spans 4 GiB or more, it enqueues the two
  * passes instead.  Same
  * requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack together. */
 nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,

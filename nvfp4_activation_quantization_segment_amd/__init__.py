@@ -128,18 +128,43 @@ def make_segments(row_start, shift: torch.Tensor, scale: torch.Tensor):
     return seg, (rs, shift, scale)
 
 
-_workspaces: dict[int, torch.Tensor] = {}
+_workspaces: dict[tuple[int, int], torch.Tensor] = {}
 
 
-def workspace(device=None) -> torch.Tensor:
-    """Per-device zero-filled absmax workspace (left zeroed by every call)."""
+def _torch_stream(stream, dev: torch.device):
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
+def workspace(device=None, stream=None) -> torch.Tensor:
+    """The producers' workspace for one (device, stream) pair, zero-filled on
+    that stream when first made.  Calls on one stream run in order and may
+    share a workspace; calls that may overlap must not (their maxima and
+    barrier words would mix), so every stream gets its own.  After a grid
+    barrier that gave up (NaN tensor scale), reset_workspaces() zero-fills
+    them again."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    idx = dev.index if dev.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(idx)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    ts = _torch_stream(stream, dev)
+    key = (dev.index, int(ts.cuda_stream))
+    ws = _workspaces.get(key)
     if ws is None:
-        ws = torch.zeros(int(lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
-        _workspaces[idx] = ws
+        with torch.cuda.stream(ts):
+            ws = torch.zeros(int(lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
     return ws
+
+
+def reset_workspaces() -> None:
+    """Zero-fill every workspace made by workspace() (synchronizes the devices)."""
+    for (idx, _), ws in _workspaces.items():
+        torch.cuda.synchronize(idx)
+        ws.zero_()
+        torch.cuda.synchronize(idx)
 
 
 def padded_rows(m: int) -> int:
@@ -273,9 +298,9 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
     q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
     if single_pass:
-        nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, q, s, m_pad, stream)
+        nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev, stream), ts, amax, q, s, m_pad, stream)
     else:
-        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev), ts, amax, stream)
+        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev, stream), ts, amax, stream)
         nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, stream)
     del keep
     return q, s, ts, amax
@@ -299,9 +324,9 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, com
     s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
     up = gu.data_ptr() + F * gu.element_size()
     if combined:
-        nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, q, s, m_pad, stream)
+        nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev, stream), ts, amax, q, s, m_pad, stream)
     else:
-        nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev), ts, amax, stream)
+        nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev, stream), ts, amax, stream)
         nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, stream)
     return q, s, ts, amax
 
@@ -318,7 +343,7 @@ def quantize(x: torch.Tensor, m_pad: int | None = None, stream=None):
     amax = torch.empty(1, dtype=torch.float32, device=dev)
     q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
-    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev), ts, amax, q, s, m_pad, stream)
+    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev, stream), ts, amax, q, s, m_pad, stream)
     return q, s, ts, amax
 
 

@@ -255,6 +255,36 @@ def test_non_default_stream(m):
         assert host(gts)[0] == s_g
 
 
+def test_two_streams_get_their_own_workspaces(m):
+    """The convenience calls on two streams, enqueued back to back with no
+    synchronization between them (the two-pass path, which has no grid
+    barrier): each stream has its own workspace, so the two tensors' maxima
+    never mix; both results match the oracle."""
+    dev = device()
+    rng = np.random.default_rng(11)
+    M, D = 3000, 512
+    xs = [bf16_np(a * rng.standard_normal((M, D))) for a in (1.0, 40.0)]
+    rs = [0, 1000, M]
+    sh = bf16_np(0.1 * rng.standard_normal((2, D)))
+    sc = bf16_np(0.1 * rng.standard_normal((2, D)))
+    seg = oracle.Segments(rs, sh, sc)
+    want = [_par.modulate_quantize(x, seg, oracle.padded_rows(M)) for x in xs]
+    xd = [to_dev_u16(x) for x in xs]
+    shd, scd = to_dev_u16(sh), to_dev_u16(sc)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    assert m.workspace(dev, streams[0]).data_ptr() != m.workspace(dev, streams[1]).data_ptr()
+    for rep in range(3):
+        got = []
+        for x, st in zip(xd, streams):
+            with torch.cuda.stream(st):
+                got.append(m.modulate_quantize(x, rs, shd, scd, stream=st, single_pass=False))
+        torch.cuda.synchronize()
+        for (gq, gs, gts, gamax), (s_g, q, s, amax) in zip(got, want):
+            assert host(gts)[0] == s_g and host(gamax)[0] == amax, rep
+            assert np.array_equal(host(gs), s) and np.array_equal(host(gq), q), rep
+
+
 def test_single_launch_without_amax_output(m):
     """nvfp4_modulate_quantize with amax_out = NULL writes the same bytes."""
     w = synth.workload("tiny")

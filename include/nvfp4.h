@@ -91,14 +91,29 @@ typedef struct {
  * "FC2 NVFP4 Library Scheduling", Exact Operation). */
 int64_t nvfp4_padded_rows(int64_t m);
 
-/* Bytes of device workspace the absmax passes and nvfp4_modulate_quantize
- * need (8,448: the global maximum and a counter of the two-pass kernels, and
- * the single launch's generation word, result word and one arrival word per
+/* Bytes of device workspace the absmax passes and the single launches need
+ * (16,640: the global maximum and a counter of the two-pass kernels, and the
+ * single launch's result word and one arrival word and one claim word per
  * workgroup).  The workspace must be zero-filled before its first use; after
  * that any sequence of calls may reuse it without clearing (the two-pass
  * kernels return their words to zero, the single launch tags its words with
- * a generation count).  It must not be shared by calls that may overlap. */
+ * a tag no earlier launch in the process used).  It must not be shared by
+ * calls that may overlap. */
 size_t nvfp4_absmax_workspace_bytes(void);
+
+/* Sets the bound on the single launches' grid-barrier wait, in microseconds
+ * (default 1,000,000), for launches enqueued from then on; returns the
+ * previous bound.  A launch whose wait passes the bound completes with a NaN
+ * tensor scale and amax, scale code 0x7F and zero codes in every block; 0
+ * makes every single launch do so at once (a way to test that path). */
+uint64_t nvfp4_set_barrier_timeout_us(uint64_t microseconds);
+
+/* Sets how long a workgroup of a single launch waits at the grid barrier
+ * before it computes the pass 1 of workgroups that have not arrived, in
+ * microseconds (default 100), for launches enqueued from then on; returns the
+ * previous value.  Results do not depend on it; 0 makes every workgroup help
+ * from its arrival on (a way to test the helping path). */
+uint64_t nvfp4_set_barrier_help_us(uint64_t microseconds);
 
 /* Pass 1 of the modulation producer ("NVFP4 Modulation Producer Fusion",
  * Dataflow, prototype step 1; "NVFP4 Streaming Design", Numerical Constraint,
@@ -133,16 +148,17 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
  * the rows each workgroup visited last from registers and LDS instead of
  * reading x again.  Writes *tensor_scale, *amax_out (may be NULL), qdata and
  * sfa as the two calls do; uses the same workspace.  The barrier needs every
- * workgroup resident; if kernels on other streams keep compute units occupied
- * so long that its wait passes 1 s, the call completes with a NaN tensor
- * scale and amax, scale code 0x7F and zero codes in every block, and so does
- * every later single-launch call on that workspace until it is zero-filled
- * again.  Where other streams may run kernels on the device at the same time,
- * use the two-pass entry points, which need no co-residency; calls that can
- * overlap in time must use different workspaces in any case.  When
- * D > 16384, or x spans 4 GiB or more, it enqueues the two
- * passes instead.  Same
- * requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack together. */
+ * workgroup's pass 1, not every workgroup's presence: workgroups that have
+ * waited 100 us (nvfp4_set_barrier_help_us) compute the pass 1 of workgroups that could not start (their
+ * CUs held by other kernels, for instance another single launch waiting at
+ * its own barrier), so concurrent launches complete; the workgroups that
+ * start late find the barrier passed.  A wait past the bound of
+ * nvfp4_set_barrier_timeout_us (1 s by default) gives a NaN tensor scale and
+ * amax, scale code 0x7F and zero codes in every block, for that call only.
+ * Calls that can overlap in time must use different workspaces.  When
+ * D > 16384, or x spans 4 GiB or more, it enqueues the two passes instead.
+ * Same requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack
+ * together. */
 nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
                                      const nvfp4_segments* seg, void* workspace, float* tensor_scale,
                                      float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
@@ -179,8 +195,8 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
  * followed by nvfp4_swiglu_pack, byte for byte): after the silu table fill,
  * one launch runs pass 1, a grid barrier and pass 2, keeping h of the rows
  * each workgroup visited last in registers, as nvfp4_modulate_quantize does
- * (same workspace, same barrier and the same failure mode when other streams
- * keep compute units occupied past 1 s).  When F > 16384, or gate/up spans
+ * (same workspace, the same barrier with helping, the same bound).  When
+ * F > 16384, or gate/up spans
  * 4 GiB or more, it enqueues the two passes instead.  Same arguments,
  * requirements and errors as the two calls together. */
 nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int64_t M, int64_t F,

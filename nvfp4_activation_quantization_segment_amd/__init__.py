@@ -55,6 +55,8 @@ def _load():
     sigs = {
         "nvfp4_padded_rows": (I64, [I64]),
         "nvfp4_absmax_workspace_bytes": (ctypes.c_size_t, []),
+        "nvfp4_set_barrier_timeout_us": (ctypes.c_uint64, [ctypes.c_uint64]),
+        "nvfp4_set_barrier_help_us": (ctypes.c_uint64, [ctypes.c_uint64]),
         "nvfp4_modulate_absmax": (I32, [P, I64, I64, I64, SEG, P, P, P, V]),
         "nvfp4_modulate_pack": (I32, [P, I64, I64, I64, SEG, P, P, P, I64, V]),
         "nvfp4_modulate_quantize": (I32, [P, I64, I64, I64, SEG, P, P, P, P, P, I64, V]),
@@ -143,9 +145,7 @@ def workspace(device=None, stream=None) -> torch.Tensor:
     """The producers' workspace for one (device, stream) pair, zero-filled on
     that stream when first made.  Calls on one stream run in order and may
     share a workspace; calls that may overlap must not (their maxima and
-    barrier words would mix), so every stream gets its own.  After a grid
-    barrier that gave up (NaN tensor scale), reset_workspaces() zero-fills
-    them again."""
+    barrier words would mix), so every stream gets its own."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     if dev.index is None:
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -159,12 +159,16 @@ def workspace(device=None, stream=None) -> torch.Tensor:
     return ws
 
 
-def reset_workspaces() -> None:
-    """Zero-fill every workspace made by workspace() (synchronizes the devices)."""
-    for (idx, _), ws in _workspaces.items():
-        torch.cuda.synchronize(idx)
-        ws.zero_()
-        torch.cuda.synchronize(idx)
+def set_barrier_timeout_us(microseconds: int) -> int:
+    """Bound on the single launches' grid-barrier wait (default 1 s); returns
+    the previous bound.  0 makes every single launch give up at once."""
+    return int(lib.nvfp4_set_barrier_timeout_us(int(microseconds)))
+
+
+def set_barrier_help_us(microseconds: int) -> int:
+    """Wait at the grid barrier before a workgroup computes absent workgroups'
+    pass 1 (default 100 us); returns the previous value.  0: help at once."""
+    return int(lib.nvfp4_set_barrier_help_us(int(microseconds)))
 
 
 def padded_rows(m: int) -> int:

@@ -1,6 +1,9 @@
 // C ABI of the NVFP4 producer and GEMM: argument validation, launch geometry
 // and error reporting.  Every check happens before anything is enqueued.
+#include <stdint.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "internal.h"
 
@@ -17,6 +20,13 @@ nvfp4_status hip_status(hipError_t e) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Tags of the single launches: one process-wide counter, so that no two
+// launches on any workspace share one (words of earlier launches then never
+// match), and the wait bound in microseconds.
+std::atomic<uint64_t> g_barrier_tag{0};
+std::atomic<uint64_t> g_barrier_wait_us{1000000};
+std::atomic<uint64_t> g_barrier_help_us{100};
 
 int64_t pad64(int64_t m) { return (m + 63) / 64 * 64; }
 
@@ -86,7 +96,23 @@ nvfp4_status check_outputs(const uint8_t* qdata, const uint8_t* sfa, int64_t M, 
 
 }  // namespace
 
+BarrierArgs nvfp4::next_barrier_args() {
+    constexpr uint64_t kTagMask = ((uint64_t)1 << 44) - 1;
+    uint64_t t = (g_barrier_tag.fetch_add(1) + 1) & kTagMask;
+    if (t == 0) t = (g_barrier_tag.fetch_add(1) + 1) & kTagMask;
+    BarrierArgs ba;
+    ba.tag = t;
+    const auto ticks = [](uint64_t us) { return us > UINT64_MAX / 100 ? UINT64_MAX : us * 100; };  // 100 MHz
+    ba.wait_ticks = ticks(g_barrier_wait_us.load());
+    ba.help_ticks = ticks(g_barrier_help_us.load());
+    return ba;
+}
+
 extern "C" {
+
+uint64_t nvfp4_set_barrier_timeout_us(uint64_t microseconds) { return g_barrier_wait_us.exchange(microseconds); }
+
+uint64_t nvfp4_set_barrier_help_us(uint64_t microseconds) { return g_barrier_help_us.exchange(microseconds); }
 
 int64_t nvfp4_padded_rows(int64_t m) { return m <= 0 ? 0 : pad64(m); }
 
@@ -146,7 +172,7 @@ static nvfp4_status quantize_both(const uint16_t* x, int64_t M, int64_t D, int64
     if (G > 0) {
         const RowGeo g = row_geo(M, M_pad, D, ldx, G, 1, 16);
         return hip_status(launch_modulate_quantize(x, g, sp, (uint32_t*)workspace, tensor_scale, amax_out, qdata,
-                                                   sfa, plain, s));
+                                                   sfa, plain, next_barrier_args(), s));
     }
     nvfp4_status st;
     const RowGeo g1 = row_geo(M, M, D, ldx, kAbsmaxWgs, 0, 8);
@@ -229,7 +255,8 @@ nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int
     if (G > 0) {
         const RowGeo g = row_geo(M, M_pad, F, ld, G, 1, 16);
         return hip_status(
-            launch_swiglu_quantize(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out, qdata, sfa, s));
+            launch_swiglu_quantize(gate, up, g, (uint32_t*)workspace, tensor_scale, amax_out, qdata, sfa,
+                                   next_barrier_args(), s));
     }
     const RowGeo g1 = row_geo(M, M, F, ld, kAbsmaxWgs, 0, 8);
     if ((st = hip_status(launch_swiglu_absmax(gate, up, g1, (uint32_t*)workspace, tensor_scale, amax_out, true, s))) !=

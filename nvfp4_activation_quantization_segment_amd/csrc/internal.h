@@ -40,21 +40,32 @@ hipError_t launch_modulate_absmax(const uint16_t* x, const RowGeo& g, const SegP
 hipError_t launch_modulate_pack(const uint16_t* x, const RowGeo& g, const SegParams& seg, const float* tensor_scale,
                                 uint8_t* qdata, uint8_t* sfa, bool plain, hipStream_t s);
 // Single-pass producer: one launch of at most modulate_quantize_grid()
-// workgroups, all resident at once (0 when that cannot be determined).  The
-// workspace holds one 8-byte arrival word per workgroup after 256 header bytes.
+// workgroups, as many as the device holds at once (0 when that cannot be
+// determined).  The workspace holds 256 header bytes, then one 8-byte arrival
+// word and one 8-byte claim word per workgroup.
 constexpr int kMaxDevices = 32;
 constexpr int kMaxGridSlots = 1024;
-constexpr size_t kWorkspaceBytes = 256 + 8 * kMaxGridSlots;
+constexpr size_t kWorkspaceBytes = 256 + 2 * 8 * kMaxGridSlots;
+// Per launch: a tag no earlier launch used (44 bits, not 0), the bound on the
+// grid-barrier wait and the wait after which a workgroup starts computing the
+// pass 1 of workgroups that have not arrived, both in ticks of the 100 MHz
+// real-time counter.
+struct BarrierArgs {
+    uint64_t tag;
+    uint64_t wait_ticks;
+    uint64_t help_ticks;
+};
+BarrierArgs next_barrier_args();
 int modulate_quantize_grid();
 // plain: the plain quantizer (y = x; seg is not read).
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
                                     float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
-                                    hipStream_t s);
-// Both SwiGLU passes in one launch (after the silu table fill); the grid of
-// swiglu_quantize_grid() keeps every workgroup resident.
+                                    const BarrierArgs& ba, hipStream_t s);
+// Both SwiGLU passes in one launch (after the silu table fill).
 int swiglu_quantize_grid();
 hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
-                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, hipStream_t s);
+                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                  const BarrierArgs& ba, hipStream_t s);
 // fill: enqueue the silu table fill first (each public entry point does once)
 hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
                                 float* tensor_scale, float* amax_out, bool fill, hipStream_t s);

@@ -372,9 +372,8 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 // Row groups held in registers per thread: as many as fit in 128 VGPRs beside
 // the working set without spills (the modulation keeps column parameters live).
-constexpr int hold_regs(bool plain) { return plain ? 11 : 7; }
+constexpr int hold_regs(bool plain) { return plain ? 9 : 7; }
 constexpr int kModHoldLdsBytes = 152 * 1024;  // LDS for held groups (modulation)
-constexpr uint64_t kBarrierTicks = 100000000;  // wait bound: 1 s of the 100 MHz real-time counter
 
 // Column parameters of one 16-column block as bf16 pairs: bf16(scale+1) and
 // shift of columns 2j (low half) and 2j+1 (high half).
@@ -429,29 +428,39 @@ __device__ __forceinline__ int seg_find(const SegParams& seg, int64_t r, int s) 
 // Workgroup maximum, then the grid barrier of the single launch.
 //
 // Workspace layout: 32-bit words 0 and 1 belong to the two-pass absmax
-// kernels; the single launch uses a generation word (64-bit, byte 64), a
-// result word (64-bit, byte 128) and one arrival word per workgroup (64-bit,
-// from byte 256).  Result and arrival words carry a 44-bit generation tag
-// above a 20-bit payload.  A call reads the generation e at its start and
-// works with tag e+1:
-//  - arrival: each workgroup stores (e+1, its maximum) into its own word, so
+// kernels; the single launch uses a result word (64-bit, byte 128), one
+// arrival word per workgroup (64-bit, from byte 256) and one claim word per
+// workgroup (after the arrival words).  These carry a 44-bit tag above a
+// 20-bit payload, and every launch gets a fresh tag from the host, so words
+// of earlier launches never match and nothing is ever reset.
+//  - arrival: each workgroup stores (tag, its maximum) into its own word, so
 //    no two workgroups contend for one word (same-address atomics serialize
 //    at ~0.1 us each, which made a counter-based barrier cost 20 us);
-//  - workgroup 0 polls every arrival word until all carry tag e+1, forms the
-//    maximum, publishes (e+1, published, bits) into the result word with a
-//    compare-and-swap, then stores generation e+1 for the next call;
-//  - the other workgroups poll the result word for tag e+1.
-// Nothing is ever reset: stale words carry older tags.  A wait that runs past
-// the bound ends in an abandon, also by compare-and-swap on the result word,
-// so exactly one outcome is visible to every workgroup: the true maximum, or
-// NaN.  An abandon does not advance the generation, so later calls on the
-// workspace find the abandoned result of their tag and also yield NaN, until
-// the caller zero-fills the workspace again.
-constexpr int kGenQword = 8;       // 64-bit word index (byte 64)
-constexpr int kResultQword = 16;   // 64-bit word index (byte 128)
-constexpr int kSlotQword = 32;     // 64-bit word index of workgroup 0's arrival word (byte 256)
+//  - workgroup 0 polls every arrival word until all carry the tag, forms the
+//    maximum and publishes (tag, published, bits) into the result word with a
+//    compare-and-swap; the other workgroups poll the result word;
+//  - helping: the barrier needs every workgroup's pass 1, not every
+//    workgroup's presence.  A workgroup that has waited `help_ticks` (the CUs
+//    it waits for may be held by another launch that waits in turn) scans
+//    the arrival words like workgroup 0, claims a workgroup that has not
+//    arrived (compare-and-swap on its claim word) and computes that
+//    workgroup's pass-1 maximum itself, storing it as its arrival.  The
+//    workgroups that could not run find the result published when they do,
+//    and go on to their pass 2;
+//  - bound: a wait past `wait_ticks` (0: at once) abandons the barrier, also
+//    by compare-and-swap on the result word, so exactly one outcome is
+//    visible to every workgroup: the true maximum, or NaN.
+// Every workgroup that settles the result word writes the tensor scale of
+// the outcome that holds (the same value for all of them).
+// The LDS flags thread 0 sets (s_done, s_scan, s_help) are read by every wave
+// between the workgroup barrier after the write and the one before the next
+// write, so all waves take the same branch and meet the same barriers.
+constexpr int kResultQword = 16;                        // 64-bit word index (byte 128)
+constexpr int kSlotQword = 32;                          // workgroup 0's arrival word (byte 256)
+constexpr int kClaimQword = kSlotQword + kMaxGridSlots;  // workgroup 0's claim word
 constexpr uint32_t kPublished = 0x10000u, kAbandoned = 0x20000u;
 constexpr uint32_t kNanBits = 0x7FC0u;
+static_assert(kClaimQword * 8 + 8 * kMaxGridSlots == kWorkspaceBytes, "workspace layout");
 
 __device__ __forceinline__ uint64_t load_dev64(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -490,82 +499,117 @@ __device__ __forceinline__ uint64_t settle(uint64_t* res, uint64_t tag, uint64_t
     return cur;
 }
 
-// The generation this call works under, read once by thread 0 at the start.
-__device__ __forceinline__ uint64_t grid_generation(const uint32_t* ws) {
-    return threadIdx.x == 0 ? load_dev64(reinterpret_cast<const uint64_t*>(ws) + kGenQword) : 0u;
-}
-
-__device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, uint64_t gen, float* tensor_scale,
-                                     float* amax_out) {
-    __shared__ uint32_t red[16];
-    __shared__ uint32_t result;
-    __shared__ uint64_t tag_s;
-    uint64_t* q = reinterpret_cast<uint64_t*>(ws);
+// Maximum of one value per thread over the workgroup (all threads get it).
+__device__ __forceinline__ uint32_t workgroup_max(uint32_t v, uint32_t* red) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nwv = (blockDim.x + 63) >> 6;
-    m16 = wave_max_u32(m16);
-    if (lane == 0) red[wv] = m16;
+    v = wave_max_u32(v);
     __syncthreads();
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    uint32_t mm = 0;
+    for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
+    return mm;
+}
+
+// The barrier.  m16: this thread's part of the workgroup's pass-1 maximum
+// (bf16 magnitude bits).  help(w) returns this thread's part of workgroup w's
+// pass-1 maximum, computed by the calling workgroup (all its threads call it).
+template <typename HELP>
+__device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, const BarrierArgs& ba, float* tensor_scale,
+                                     float* amax_out, HELP help) {
+    __shared__ uint32_t red[16];
+    __shared__ uint32_t s_result;
+    __shared__ int s_done, s_scan, s_helping, s_cand, s_help;
+    __shared__ uint64_t s_t0;
+    uint64_t* q = reinterpret_cast<uint64_t*>(ws);
+    const int G = (int)gridDim.x;
+    const uint64_t tag = ba.tag;
+    const int rot0 = (int)blockIdx.x + G / 2;  // helpers start half the grid away from themselves
+    const uint32_t mm = workgroup_max(m16, red);
     if (threadIdx.x == 0) {
-        uint32_t mm = 0;
-        for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
-        tag_s = gen + 1u;
-        store_dev64(&q[kSlotQword + blockIdx.x], tagged(gen + 1u, mm));
+        store_dev64(&q[kSlotQword + blockIdx.x], tagged(tag, mm));
+        s_t0 = __builtin_amdgcn_s_memrealtime();
+        s_done = 0;
+        s_scan = blockIdx.x == 0;
+        s_helping = 0;
     }
-    if (blockIdx.x == 0) {
+    __syncthreads();
+    int next = threadIdx.x;  // this thread's first arrival word not yet seen with the tag
+    uint32_t mine = 0;       // maximum of the arrival words this thread has seen
+    for (;;) {
+        // published or abandoned already?
+        if (threadIdx.x == 0) {
+            const uint64_t r = load_dev64(&q[kResultQword]);
+            if (tag_of(r) == tag) {
+                s_result = outcome_bits(r);
+                s_done = 1;
+            }
+        }
         __syncthreads();
-        const uint64_t tag = tag_s;
-        // every thread polls its share of the arrival words
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        uint32_t mine = 0;
-        int next = threadIdx.x;
-        bool late = false;  // uniform over the workgroup
-        for (;;) {
-            while (next < (int)gridDim.x) {
+        if (s_done) break;
+        // workgroup 0 and helpers: have all arrived?
+        if (s_scan) {
+            while (next < G) {
                 const uint64_t v = load_dev64(&q[kSlotQword + next]);
                 if (tag_of(v) != tag) break;
                 mine = ((uint32_t)v & 0xFFFFu) > mine ? ((uint32_t)v & 0xFFFFu) : mine;
                 next += blockDim.x;
             }
-            if (__syncthreads_and(next >= (int)gridDim.x)) break;
-            if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks)) {
-                late = true;
+            if (__syncthreads_and(next >= G)) {
+                const uint32_t all = workgroup_max(mine, red);
+                if (threadIdx.x == 0) {
+                    const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kPublished | all));
+                    write_scale(outcome_bits(r), tensor_scale, amax_out);
+                    s_result = outcome_bits(r);
+                }
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
         }
-        mine = wave_max_u32(mine);
-        __syncthreads();
-        if (lane == 0) red[wv] = mine;
-        __syncthreads();
+        __syncthreads();  // s_done and s_scan read by every wave
+        // the bound; from help_ticks on, help a workgroup that has not arrived
         if (threadIdx.x == 0) {
-            uint32_t mm = 0;
-            for (int i = 0; i < nwv; ++i) mm = red[i] > mm ? red[i] : mm;
-            const uint64_t want = tagged(tag, late ? kAbandoned : (kPublished | mm));
-            const uint64_t r = settle(&q[kResultQword], tag, want);
-            // the outcome that holds, also when an abandon got there first
-            // (then every writer writes the same NaN)
-            write_scale(outcome_bits(r), tensor_scale, amax_out);
-            if (r == want && !late) store_dev64(&q[kGenQword], tag);
-            result = outcome_bits(r);
-        }
-    } else if (threadIdx.x == 0) {
-        const uint64_t tag = gen + 1u;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        uint64_t r;
-        while (tag_of(r = load_dev64(&q[kResultQword])) != tag) {
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
-                const uint64_t want = tagged(tag, kAbandoned);
-                r = settle(&q[kResultQword], tag, want);
-                if (r == want) write_scale(kNanBits, tensor_scale, amax_out);
-                break;
+            const uint64_t el = __builtin_amdgcn_s_memrealtime() - s_t0;
+            s_help = -1;
+            s_cand = G;
+            if (ba.wait_ticks == 0 || el > ba.wait_ticks) {
+                const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kAbandoned));
+                write_scale(outcome_bits(r), tensor_scale, amax_out);
+                s_result = outcome_bits(r);
+                s_done = 1;
+            } else if (el >= ba.help_ticks) {
+                s_scan = 1;
+                s_helping = 1;
             }
+        }
+        __syncthreads();
+        if (s_done) break;
+        if (s_helping) {
+            // every thread offers the first arrival word it has not seen with
+            // the tag, if that workgroup is still absent and unclaimed; the
+            // offer first in rotation order from rot0 is claimed
+            if (next < G && tag_of(load_dev64(&q[kSlotQword + next])) != tag &&
+                tag_of(load_dev64(&q[kClaimQword + next])) != tag)
+                atomicMin(&s_cand, (next - rot0 + 2 * G) % G);
+            __syncthreads();
+            if (threadIdx.x == 0 && s_cand < G) {
+                const int w = (s_cand + rot0) % G;
+                const uint64_t c = load_dev64(&q[kClaimQword + w]);
+                if (tag_of(c) != tag && cas_dev64(&q[kClaimQword + w], c, tagged(tag, 1u)) == c) s_help = w;
+            }
+            __syncthreads();
+        }
+        const int w = s_help;
+        if (w >= 0) {
+            const uint32_t hm = workgroup_max(help(w), red);
+            if (threadIdx.x == 0) store_dev64(&q[kSlotQword + w], tagged(tag, hm));
+        } else {
             __builtin_amdgcn_s_sleep(2);
         }
-        result = outcome_bits(r);
+        __syncthreads();  // s_done, s_helping and s_help read by every wave
     }
     __syncthreads();
-    return result;
+    return s_result;
 }
 
 // Per-workgroup split of its nw row groups: ns streamed (re-read in pass 2),
@@ -868,7 +912,8 @@ template <bool PLAIN>
 __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t* __restrict__ x, RowGeo g,
                                                                  SegParams seg, uint32_t* ws, float* tensor_scale,
                                                                  float* amax_out, uint8_t* __restrict__ qdata,
-                                                                 uint8_t* __restrict__ sfa, int hold_lds) {
+                                                                 uint8_t* __restrict__ sfa, int hold_lds,
+                                                                 BarrierArgs ba) {
     __shared__ uint4 hold[kModHoldLdsBytes / 16];
     __shared__ float2 dr[128];
     const char* xb = reinterpret_cast<const char*>(x);
@@ -881,7 +926,6 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     const int gstride = (int)gridDim.x * g.R;
     const int r_first = (int)blockIdx.x * g.R + rho;  // row of local group 0
     const uint32_t xrow = 2u * (uint32_t)g.ldx, xcol = 32u * (uint32_t)b;
-    const uint64_t gen = grid_generation(ws);
 
     // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
     uint32_t m2 = 0;
@@ -990,7 +1034,42 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             if (valid) max16(m2, hy[h]);
         }
     }
-    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, gen, tensor_scale, amax_out);
+    // pass 1 of workgroup w, for the barrier's helping (see grid_max_barrier);
+    // 8 columns at a time and the column parameters loaded per row, so that
+    // it needs few registers beside the held rows
+    auto help = [=, &seg](int w) -> uint32_t {
+        uint32_t hm2 = 0;
+        if (on) {
+            const int wf = w * g.R + rho;
+            const int nwm = w < groups ? (int)((groups - 1 - w) / gridDim.x + 1) : 0;
+            int hs2 = 0;
+            for (int t2 = 0; t2 < nwm; ++t2) {
+                const int r = wf + t2 * gstride;
+                if (r >= g.M) break;
+                if constexpr (!PLAIN) hs2 = seg_find(seg, r, hs2);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint4 a = ld16o(xb, (uint32_t)r * xrow + xcol + 16u * half);
+                    uint32_t y[4] = {a.x, a.y, a.z, a.w};
+                    if constexpr (!PLAIN) {
+                        const uint16_t* sc = seg.scale + (int64_t)hs2 * seg.ld + 16 * b + 8 * half;
+                        const uint16_t* sh = seg.shift + (int64_t)hs2 * seg.ld + 16 * b + 8 * half;
+                        const uint4 c4 = ld16(sc), h4 = ld16(sh);
+                        const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+                        const uint32_t hw[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            y[j] = modulate2r(y[j], mod_scale1((uint16_t)(cw[j] & 0xFFFFu)),
+                                              mod_scale1((uint16_t)(cw[j] >> 16)), bf16_lo(hw[j]), bf16_hi(hw[j]));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hm2 = pk_max_u16(hm2, mag2(y[j]));
+                }
+            }
+        }
+        return fold_max(hm2);
+    };
+    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, ba, tensor_scale, amax_out, help);
 
     // ---- pass 2 ----
     const float amax = __uint_as_float(bits << 16);
@@ -1011,7 +1090,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
 // those first and reads gate and up again for the rest, last to first.  The
 // silu table is filled by silu_lut_fill_kernel before the launch.
 // ---------------------------------------------------------------------------
-constexpr int kSwigluHoldRegs = 11;  // row groups held in registers per thread (123 VGPRs, no spills)
+constexpr int kSwigluHoldRegs = 9;  // row groups held in registers per thread
 
 // h of 16 columns as packed bf16 words (the pass-1 form, also what is held).
 __device__ __forceinline__ void swiglu16_pk(const uint16_t* lut, const uint4& g0, const uint4& g1, const uint4& u0,
@@ -1024,10 +1103,9 @@ __global__ __launch_bounds__(1024) void swiglu_quantize_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ up, RowGeo g,
                                                                uint32_t* ws, float* tensor_scale, float* amax_out,
                                                                uint8_t* __restrict__ qdata,
-                                                               uint8_t* __restrict__ sfa) {
+                                                               uint8_t* __restrict__ sfa, BarrierArgs ba) {
     __shared__ __attribute__((aligned(16))) uint16_t slut[65536];
     __shared__ float2 dr[128];
-    const uint64_t gen = grid_generation(ws);
     lut_to_lds(slut);
     const char* gb = reinterpret_cast<const char*>(gate);
     const char* ub = reinterpret_cast<const char*>(up);
@@ -1064,7 +1142,28 @@ __global__ __launch_bounds__(1024) void swiglu_quantize_kernel(const uint16_t* _
             }
         }
     }
-    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, gen, tensor_scale, amax_out);
+    // pass 1 of workgroup w, for the barrier's helping (see grid_max_barrier)
+    auto help = [=](int w) -> uint32_t {
+        uint32_t hm2 = 0;
+        if (on) {
+            const int wf = w * g.R + rho;
+            const int nwm = w < groups ? (int)((groups - 1 - w) / gridDim.x + 1) : 0;
+            for (int t2 = 0; t2 < nwm; ++t2) {
+                const int r = wf + t2 * gstride;
+                if (r >= g.M) break;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t o = (uint32_t)r * xrow + xcol + 16u * half;
+                    uint32_t h[4];
+                    swiglu8(slut, ld16o(gb, o), ld16o(ub, o), h);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hm2 = pk_max_u16(hm2, mag2(h[j]));
+                }
+            }
+        }
+        return fold_max(hm2);
+    };
+    const uint32_t bits = grid_max_barrier(fold_max(m2), ws, ba, tensor_scale, amax_out, help);
 
     // ---- pass 2 ----
     const float amax = __uint_as_float(bits << 16);
@@ -1260,10 +1359,11 @@ int swiglu_quantize_grid() {
 }
 
 hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, const RowGeo& g, uint32_t* ws,
-                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, hipStream_t s) {
+                                  float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa,
+                                  const BarrierArgs& ba, hipStream_t s) {
     launch_silu_fill(s);
     hipLaunchKernelGGL(swiglu_quantize_kernel, dim3(g.grid), dim3(g.block), 0, s, gate, up, g, ws, tensor_scale,
-                       amax_out, qdata, sfa);
+                       amax_out, qdata, sfa, ba);
     return hipGetLastError();
 }
 
@@ -1273,14 +1373,14 @@ hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, cons
 // API would guarantee residency but costs tens of microseconds per launch.
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
                                     float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
-                                    hipStream_t s) {
+                                    const BarrierArgs& ba, hipStream_t s) {
     const int hold_lds = kModHoldLdsBytes / (32 * g.block);
     if (plain)
         hipLaunchKernelGGL(modulate_quantize_kernel<true>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
-                           tensor_scale, amax_out, qdata, sfa, hold_lds);
+                           tensor_scale, amax_out, qdata, sfa, hold_lds, ba);
     else
         hipLaunchKernelGGL(modulate_quantize_kernel<false>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
-                           tensor_scale, amax_out, qdata, sfa, hold_lds);
+                           tensor_scale, amax_out, qdata, sfa, hold_lds, ba);
     return hipGetLastError();
 }
 

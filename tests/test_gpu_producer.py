@@ -153,13 +153,12 @@ def test_workspace_reuse_between_calls(m):
     """Calls in a row on one workspace, alternating the single launch and the
     two passes: each sees only its own tensor (the maxima differ).  The two
     passes leave their words at zero; the single launch tags its words with a
-    generation count, which advances by one per call."""
+    tag of its own, so it needs no clearing either."""
     dev = device()
     rs = [0, 64]
     sh = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
     sc = torch.zeros((1, 64), dtype=torch.bfloat16, device=dev)
     ws = torch.zeros(int(m.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
-    gen = 0
     for single in (True, False, True, True):
         for val in (100.0, 2.0, 37.0):
             t = torch.full((64, 64), val, dtype=torch.bfloat16, device=dev)
@@ -170,28 +169,23 @@ def test_workspace_reuse_between_calls(m):
             s = torch.empty((64, 4), dtype=torch.uint8, device=dev)
             if single:
                 m.nvfp4_modulate_quantize(t, 64, 64, 64, seg, ws, ts, a, q, s, 64)
-                gen += 1
             else:
                 m.nvfp4_modulate_absmax(t, 64, 64, 64, seg, ws, ts, a)
                 m.nvfp4_modulate_pack(t, 64, 64, 64, seg, ts, q, s, 64)
             torch.cuda.synchronize()
             assert host(a)[0] == val
             assert host(ts)[0] == np.float32(val) / np.float32(2688.0)
-            w = host(ws)
-            assert not w[:8].any()
-            assert int(w[64:72].view(np.uint64)[0]) == gen
+            assert not host(ws)[:8].any()
 
 
-def test_abandoned_barrier_is_sticky_until_the_workspace_is_zeroed(m):
+def test_barrier_timeout_gives_nan_for_that_call_only(m):
     """The failure path of the single launches' grid barrier, forced from the
-    host without any wait: the workspace's result word is preset to an
-    abandoned barrier of the next generation (what a wait past its bound
-    leaves behind).  Every single-launch call on that workspace, modulation
-    and SwiGLU, then completes with a NaN tensor scale and amax, scale code
-    0x7F in every block and zero codes (padding rows zero), and leaves the
-    generation where it was; after a zero fill the next call is exact again.
-    White-box: the test writes the generation word (bytes 64..71) and the
-    result word (bytes 128..135) as (tag << 20) | 0x20000."""
+    host with a wait bound of 0 (every single launch gives up at once):
+    modulation and SwiGLU calls complete with a NaN tensor scale and amax,
+    scale code 0x7F in every block and zero codes (padding rows zero).  With
+    the default bound restored, the next call on the same workspace is exact
+    (every launch carries its own tag, so nothing of the abandoned one
+    lingers)."""
     dev = device()
     rng = np.random.default_rng(7)
     M, D = 130, 256
@@ -201,41 +195,114 @@ def test_abandoned_barrier_is_sticky_until_the_workspace_is_zeroed(m):
     sc = bf16_np(0.1 * rng.standard_normal((2, D)))
     gu = bf16_np(2 * rng.standard_normal((M, 2 * D)))
     ws = torch.zeros(int(m.lib.nvfp4_absmax_workspace_bytes()), dtype=torch.uint8, device=dev)
-    gen = 5
-    words = ws.view(torch.int64)
-    words[8] = gen
-    words[16] = ((gen + 1) << 20) | 0x20000
     m_pad = oracle.padded_rows(M)
     seg, keep = m.make_segments(rs, to_dev_u16(sh), to_dev_u16(sc))
-    for kind in ("modulate", "swiglu", "modulate"):
-        ts = torch.zeros(1, dtype=torch.float32, device=dev)
-        a = torch.zeros(1, dtype=torch.float32, device=dev)
-        q = torch.full((m_pad, D // 2), 0x55, dtype=torch.uint8, device=dev)
-        s = torch.full((m_pad, D // 16), 0x55, dtype=torch.uint8, device=dev)
-        if kind == "modulate":
-            m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
-        else:
-            g = to_dev_u16(gu)
-            m.nvfp4_swiglu_quantize(g, g.data_ptr() + 2 * D, M, D, 2 * D, ws, ts, a, q, s, m_pad)
-        torch.cuda.synchronize()
-        assert np.isnan(host(ts)[0]) and np.isnan(host(a)[0]), kind
-        hs, hq = host(s), host(q)
-        assert (hs[:M] == 0x7F).all() and not hs[M:].any(), kind
-        assert not hq.any(), kind
-        assert int(host(words)[8]) == gen, kind
-    ws.zero_()
-    ts = torch.zeros(1, dtype=torch.float32, device=dev)
-    a = torch.zeros(1, dtype=torch.float32, device=dev)
-    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
-    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+
+    def outputs():
+        return (torch.zeros(1, dtype=torch.float32, device=dev), torch.zeros(1, dtype=torch.float32, device=dev),
+                torch.full((m_pad, D // 2), 0x55, dtype=torch.uint8, device=dev),
+                torch.full((m_pad, D // 16), 0x55, dtype=torch.uint8, device=dev))
+
+    previous = m.set_barrier_timeout_us(0)
+    try:
+        for kind in ("modulate", "swiglu", "modulate"):
+            ts, a, q, s = outputs()
+            if kind == "modulate":
+                m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
+            else:
+                g = to_dev_u16(gu)
+                m.nvfp4_swiglu_quantize(g, g.data_ptr() + 2 * D, M, D, 2 * D, ws, ts, a, q, s, m_pad)
+            torch.cuda.synchronize()
+            assert np.isnan(host(ts)[0]) and np.isnan(host(a)[0]), kind
+            hs, hq = host(s), host(q)
+            assert (hs[:M] == 0x7F).all() and not hs[M:].any(), kind
+            assert not hq.any(), kind
+    finally:
+        assert m.set_barrier_timeout_us(previous) == 0
+    ts, a, q, s = outputs()
     m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
     torch.cuda.synchronize()
     s_g, oq, os_, amax = _par.modulate_quantize(x, oracle.Segments(rs, sh, sc), m_pad)
     assert host(ts)[0] == s_g and host(a)[0] == amax
     assert np.array_equal(host(s), os_), first_mismatch(host(s), os_)
     assert np.array_equal(host(q), oq), first_mismatch(host(q), oq)
-    assert int(host(words)[8]) == 1
     del keep
+
+
+@pytest.mark.parametrize("kind", ["modulate", "plain", "swiglu"])
+def test_helping_from_arrival_is_exact(m, kind):
+    """With a help delay of 0 every workgroup, once it has reached the grid
+    barrier, claims workgroups that have not arrived and computes their pass
+    1 itself (the path taken when another kernel holds the CUs those
+    workgroups need).  The maxima it stores are the ones those workgroups
+    store, so every call is byte-exact, whether the shapes give each
+    workgroup one row group or several, and with ragged segments."""
+    rng = np.random.default_rng(23)
+    previous = m.set_barrier_help_us(0)
+    try:
+        for M, D in ((1, 16), (700, 5376), (3001, 7168), (20011, 1056)):
+            if kind == "swiglu":
+                gu = bf16_np(2 * rng.standard_normal((M, 2 * D)))
+                check_swiglu(m, gu)
+            elif kind == "plain":
+                check_plain(m, bf16_np(rng.standard_normal((M, D)) * np.exp(rng.standard_normal((M, 1)))))
+            else:
+                x = bf16_np(3 * rng.standard_normal((M, D)))
+                rs = sorted({0, M, *(int(r) for r in rng.integers(0, M, 3))})
+                ns = len(rs) - 1
+                sh = bf16_np(0.1 * rng.standard_normal((ns, D)))
+                sc = bf16_np(0.1 * rng.standard_normal((ns, D)))
+                check_modulate(m, x, rs, sh, sc)
+    finally:
+        assert m.set_barrier_help_us(previous) == 0
+
+
+def test_concurrent_single_launches_on_two_streams(m):
+    """Two single-launch producers (modulation and SwiGLU) on two streams,
+    enqueued behind a long matrix product on a third stream so that they
+    start together and compete for the CUs.  Each needs all its workgroups'
+    pass 1 before its barrier passes; workgroups that wait compute the pass 1
+    of those that could not start, so both complete, exactly, and well inside
+    the barrier's 1 s bound."""
+    dev = device()
+    rng = np.random.default_rng(19)
+    M, D = 12000, 5376
+    x = bf16_np(rng.standard_normal((M, D)))
+    gu = bf16_np(2 * rng.standard_normal((M // 4, 2 * 3584)))
+    rs = [0, 9000, M]
+    sh = bf16_np(0.1 * rng.standard_normal((2, D)))
+    sc = bf16_np(0.1 * rng.standard_normal((2, D)))
+    want_mod = _par.modulate_quantize(x, oracle.Segments(rs, sh, sc), oracle.padded_rows(M))
+    want_sw = _par.swiglu_quantize(gu, oracle.padded_rows(M // 4))
+    xd, gud, shd, scd = to_dev_u16(x), to_dev_u16(gu), to_dev_u16(sh), to_dev_u16(sc)
+    big = torch.randn((8192, 8192), device=dev)
+    s0, s1, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s0):
+            for _ in range(4):
+                big = big @ big * 1e-4
+        events = []
+        with torch.cuda.stream(s1):
+            a1 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            a1.record(s1)
+            got_mod = m.modulate_quantize(xd, rs, shd, scd, stream=s1)
+            b1.record(s1)
+        with torch.cuda.stream(s2):
+            a2 = torch.cuda.Event(enable_timing=True)
+            b2 = torch.cuda.Event(enable_timing=True)
+            a2.record(s2)
+            got_sw = m.swiglu_quantize(gud, stream=s2)
+            b2.record(s2)
+        torch.cuda.synchronize()
+        ms = (a1.elapsed_time(b1), a2.elapsed_time(b2))
+        print(f"rep {rep}: {ms[0]:.2f} ms, {ms[1]:.2f} ms", flush=True)
+        for (gq, gs, gts, gamax), (s_g, q, s, amax), name in ((got_mod, want_mod, "modulation"),
+                                                             (got_sw, want_sw, "swiglu")):
+            assert host(gts)[0] == s_g and host(gamax)[0] == amax, (rep, name)
+            assert np.array_equal(host(gs), s) and np.array_equal(host(gq), q), (rep, name)
+        assert max(ms) < 500.0, ms
 
 
 def test_non_default_stream(m):

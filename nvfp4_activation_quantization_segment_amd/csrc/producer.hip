@@ -1038,6 +1038,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     // 8 columns at a time and the column parameters loaded per row, so that
     // it needs few registers beside the held rows
     auto help = [=, &seg](int w) -> uint32_t {
+        (void)seg;  // read only when modulating
         uint32_t hm2 = 0;
         if (on) {
             const int wf = w * g.R + rho;

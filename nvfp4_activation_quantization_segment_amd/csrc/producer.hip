@@ -371,7 +371,8 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
 // offset idx / C16 in a group of R rows; workgroup w visits groups w, w+G, ...
 // ---------------------------------------------------------------------------
 // Row groups held in registers per thread: as many as fit in 128 VGPRs beside
-// the working set without spills (the modulation keeps column parameters live).
+// the working set and the barrier's helper with no spill inside a loop (the
+// modulation keeps column parameters live).
 constexpr int hold_regs(bool plain) { return plain ? 9 : 7; }
 constexpr int kModHoldLdsBytes = 152 * 1024;  // LDS for held groups (modulation)
 
@@ -1091,7 +1092,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
 // those first and reads gate and up again for the rest, last to first.  The
 // silu table is filled by silu_lut_fill_kernel before the launch.
 // ---------------------------------------------------------------------------
-constexpr int kSwigluHoldRegs = 9;  // row groups held in registers per thread
+constexpr int kSwigluHoldRegs = 9;  // row groups held in registers per thread (as hold_regs)
 
 // h of 16 columns as packed bf16 words (the pass-1 form, also what is held).
 __device__ __forceinline__ void swiglu16_pk(const uint16_t* lut, const uint4& g0, const uint4& g1, const uint4& u0,

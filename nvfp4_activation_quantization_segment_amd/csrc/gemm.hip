@@ -181,11 +181,18 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
                 af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
         }
         store_part(ra, sc, j, dst0, dst1, st.hb);
+        // Four MFMAs in a row share one weight fragment, and the activation
+        // fragments run 0..3 then 3..0, so that consecutive instructions
+        // change as few operands as possible: under the power limit fewer
+        // operand changes mean a higher clock (measured 0.8% for keeping the
+        // A operand, 0.2-0.5% more for the reversed second row).
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = i ? 3 - kk : kk;
                 acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[b][i], af[b][k], acc[i][k], 0, 0, 0);
+            }
         __builtin_amdgcn_sched_barrier(0);
     }
     ra = na;
@@ -364,8 +371,10 @@ gemm_kernel(GemmArgs a, GemmPart p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int k = i ? 3 - kk : kk;
                     acc[i][k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[k], acc[i][k], 0, 0, 0);
+                }
         }
     }
 

@@ -167,3 +167,20 @@ def test_gate_residual_argument_errors(pkg):
 def test_status_strings(pkg):
     for st in range(6):
         assert pkg.lib.nvfp4_status_string(st)
+
+
+def test_barrier_settings_round_trip(pkg):
+    """The single launches' barrier settings: each setter returns the value it
+    replaces (defaults 1 s and 100 us); host state only, nothing launched."""
+    assert pkg.lib.nvfp4_absmax_workspace_bytes() == 256 + 2 * 8 * 1024
+    t0 = pkg.set_barrier_timeout_us(250)
+    h0 = pkg.set_barrier_help_us(7)
+    try:
+        assert pkg.set_barrier_timeout_us(0) == 250
+        assert pkg.set_barrier_help_us(0) == 7
+        assert pkg.set_barrier_timeout_us(2**40) == 0
+        assert pkg.set_barrier_timeout_us(1000000) == 2**40
+    finally:
+        pkg.set_barrier_timeout_us(t0)
+        pkg.set_barrier_help_us(h0)
+    assert (t0, h0) == (1000000, 100)

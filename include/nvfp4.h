@@ -164,6 +164,21 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
                                      float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
                                      void* stream);
 
+/* nvfp4_modulate_quantize for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same results, byte for byte, with no workspace argument.
+ * The grid barrier's words live in a fixed 16,640-byte array inside the
+ * library's code object, one copy per device (held until the process ends);
+ * every shape nvfp4_modulate_quantize accepts fits it.  The call enqueues a
+ * small kernel that zeroes those words, then the producer, on `stream`; it
+ * calls no allocator.  All calls on one device share the array: calls that
+ * can overlap in time on one device (two streams without ordering between
+ * them) race and must not be made.  Same arguments, requirements and errors
+ * as nvfp4_modulate_quantize, without the workspace. */
+nvfp4_status nvfp4_modulate_quantize_noalloc(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                             const nvfp4_segments* seg, float* tensor_scale, float* amax_out,
+                                             uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream);
+
 /* The plain quantizer: nvfp4_modulate_quantize with y = x (no modulation), for
  * activations that need none (the attention-output projection's input,
  * "NVFP4 Streaming Design", P0/P2: the widths 5376, 7168, 14336) and for

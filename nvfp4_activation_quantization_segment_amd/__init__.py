@@ -60,6 +60,7 @@ def _load():
         "nvfp4_modulate_absmax": (I32, [P, I64, I64, I64, SEG, P, P, P, V]),
         "nvfp4_modulate_pack": (I32, [P, I64, I64, I64, SEG, P, P, P, I64, V]),
         "nvfp4_modulate_quantize": (I32, [P, I64, I64, I64, SEG, P, P, P, P, P, I64, V]),
+        "nvfp4_modulate_quantize_noalloc": (I32, [P, I64, I64, I64, SEG, P, P, P, P, I64, V]),
         "nvfp4_quantize": (I32, [P, I64, I64, I64, P, P, P, P, P, I64, V]),
         "nvfp4_swiglu_absmax": (I32, [P, P, I64, I64, I64, P, P, P, V]),
         "nvfp4_swiglu_pack": (I32, [P, P, I64, I64, I64, P, P, P, I64, V]),
@@ -194,6 +195,12 @@ def nvfp4_modulate_quantize(x, M, D, ldx, seg, ws, tensor_scale, amax_out, qdata
     _check("nvfp4_modulate_quantize",
            lib.nvfp4_modulate_quantize(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(ws), _ptr(tensor_scale),
                                        _ptr(amax_out), _ptr(qdata), _ptr(sfa), M_pad, _stream(stream)))
+
+
+def nvfp4_modulate_quantize_noalloc(x, M, D, ldx, seg, tensor_scale, amax_out, qdata, sfa, M_pad, stream=None):
+    _check("nvfp4_modulate_quantize_noalloc",
+           lib.nvfp4_modulate_quantize_noalloc(_ptr(x), M, D, ldx, ctypes.byref(seg), _ptr(tensor_scale),
+                                               _ptr(amax_out), _ptr(qdata), _ptr(sfa), M_pad, _stream(stream)))
 
 
 def nvfp4_quantize(x, M, D, ldx, ws, tensor_scale, amax_out, qdata, sfa, M_pad, stream=None):

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 
@@ -91,6 +92,34 @@ nvfp4_status check_outputs(const uint8_t* qdata, const uint8_t* sfa, int64_t M, 
     if (!qdata || !sfa) return NVFP4_ERR_INVALID_ARGUMENT;
     if (M_pad < pad64(M)) return NVFP4_ERR_SHAPE;
     if (!aligned(qdata, 4)) return NVFP4_ERR_ALIGNMENT;
+    return NVFP4_OK;
+}
+
+// The barrier words of nvfp4_modulate_quantize_noalloc: a fixed array in the
+// code object, one copy on every device the library runs on, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): it passes the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kWorkspaceBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+nvfp4_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return NVFP4_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return NVFP4_OK;
 }
 
@@ -195,6 +224,27 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
     if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
     return quantize_both(x, M, D, ldx, sp, false, workspace, tensor_scale, amax_out, qdata, sfa, M_pad,
                          (hipStream_t)stream);
+}
+
+nvfp4_status nvfp4_modulate_quantize_noalloc(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
+                                             const nvfp4_segments* seg, float* tensor_scale, float* amax_out,
+                                             uint8_t* qdata, uint8_t* sfa, int64_t M_pad, void* stream) {
+    nvfp4_status st = check_rows(x, M, D, ldx);
+    if (st != NVFP4_OK) return st;
+    SegParams sp;
+    if ((st = check_segments(seg, M, D, &sp)) != NVFP4_OK) return st;
+    if (!tensor_scale) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(tensor_scale, 4) || !aligned(amax_out, 4)) return NVFP4_ERR_ALIGNMENT;
+    if ((st = check_outputs(qdata, sfa, M, M_pad)) != NVFP4_OK) return st;
+    // the barrier needs 256 header bytes and 16 bytes per workgroup; the grid
+    // is capped at kMaxGridSlots, so every accepted shape fits the scratch
+    const size_t need = 256 + 16 * (size_t)kMaxGridSlots;
+    if (need > sizeof(scratch)) return NVFP4_ERR_SHAPE;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != NVFP4_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if ((st = hip_status(launch_clear_workspace(ws, need, s))) != NVFP4_OK) return st;
+    return quantize_both(x, M, D, ldx, sp, false, ws, tensor_scale, amax_out, qdata, sfa, M_pad, s);
 }
 
 nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx, void* workspace,

@@ -72,6 +72,9 @@ hipError_t launch_swiglu_absmax(const uint16_t* gate, const uint16_t* up, const 
 hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const RowGeo& g, const float* tensor_scale,
                               uint8_t* qdata, uint8_t* sfa, bool fill, hipStream_t s);
 hipError_t launch_step(int which, const void* a, const void* b, const void* c, void* out, int64_t n, hipStream_t s);
+// Zero-fills `bytes` (a multiple of 16, at most 16 x 65,536) of device memory
+// with one small kernel on s.
+hipError_t launch_clear_workspace(void* ws, size_t bytes, hipStream_t s);
 
 struct GemmArgs {
     const uint8_t* qa;

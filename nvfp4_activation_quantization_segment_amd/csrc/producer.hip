@@ -1409,6 +1409,18 @@ hipError_t launch_swiglu_pack(const uint16_t* gate, const uint16_t* up, const Ro
     return hipGetLastError();
 }
 
+// Zeroes a workspace of `bytes` (a multiple of 16) with vector stores, in
+// stream order: a kernel rather than a memset, so that a call captured into a
+// graph clears the words again on every replay.
+__global__ __launch_bounds__(256) void clear_words_kernel(uint4* __restrict__ p, int n16) {
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_clear_workspace(void* ws, size_t bytes, hipStream_t s) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, s, (uint4*)ws, (int)(bytes / 16));
+    return hipGetLastError();
+}
+
 hipError_t launch_step(int which, const void* a, const void* b, const void* c, void* out, int64_t n, hipStream_t s) {
     const dim3 grid(step_grid(n)), block(256);
     switch (which) {

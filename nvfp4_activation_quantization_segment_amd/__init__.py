@@ -304,15 +304,17 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
     m_pad = padded_rows(M) if m_pad is None else m_pad
     seg, keep = make_segments(row_start, shift, scale)
     dev = x.device
-    ts = torch.empty(1, dtype=torch.float32, device=dev)
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
-    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
-    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+    st = _torch_stream(stream, dev)
+    with torch.cuda.stream(st):  # outputs belong to the stream that writes them
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
     if single_pass:
-        nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev, stream), ts, amax, q, s, m_pad, stream)
+        nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev, st), ts, amax, q, s, m_pad, st)
     else:
-        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev, stream), ts, amax, stream)
-        nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, stream)
+        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev, st), ts, amax, st)
+        nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, st)
     del keep
     return q, s, ts, amax
 
@@ -329,16 +331,18 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, com
         raise ValueError("gate/up must have unit column stride")
     m_pad = padded_rows(M) if m_pad is None else m_pad
     dev = gu.device
-    ts = torch.empty(1, dtype=torch.float32, device=dev)
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
-    q = torch.empty((m_pad, F // 2), dtype=torch.uint8, device=dev)
-    s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
+    st = _torch_stream(stream, dev)
+    with torch.cuda.stream(st):
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        q = torch.empty((m_pad, F // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
     up = gu.data_ptr() + F * gu.element_size()
     if combined:
-        nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev, stream), ts, amax, q, s, m_pad, stream)
+        nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev, st), ts, amax, q, s, m_pad, st)
     else:
-        nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev, stream), ts, amax, stream)
-        nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, stream)
+        nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev, st), ts, amax, st)
+        nvfp4_swiglu_pack(gu, up, M, F, gu.stride(0), ts, q, s, m_pad, st)
     return q, s, ts, amax
 
 
@@ -350,11 +354,13 @@ def quantize(x: torch.Tensor, m_pad: int | None = None, stream=None):
         raise ValueError("x must have unit column stride")
     m_pad = padded_rows(M) if m_pad is None else m_pad
     dev = x.device
-    ts = torch.empty(1, dtype=torch.float32, device=dev)
-    amax = torch.empty(1, dtype=torch.float32, device=dev)
-    q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
-    s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
-    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev, stream), ts, amax, q, s, m_pad, stream)
+    st = _torch_stream(stream, dev)
+    with torch.cuda.stream(st):
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
+    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev, st), ts, amax, q, s, m_pad, st)
     return q, s, ts, amax
 
 
@@ -370,16 +376,21 @@ def gemm(qa, sfa, a_scale, M: int, qw, sfw, w_scale, out: torch.Tensor | None = 
          workspace: torch.Tensor | None = None):
     """out [M, N] bf16 = bf16(a_scale * w_scale * dequant(qa) dequant(qw)^T).
 
-    Runs nvfp4_gemm_ws; a workspace of nvfp4_gemm_workspace_bytes(M, N, K)
-    bytes is allocated with torch when none is given."""
+    Runs nvfp4_gemm_ws on `stream` (default: the current stream); a workspace
+    of nvfp4_gemm_workspace_bytes(M, N, K) bytes is allocated with torch when
+    none is given.  The output and that workspace are allocated on the stream
+    the GEMM runs on, so the caching allocator hands the workspace to no other
+    stream's allocation before the GEMM has finished with it."""
     M_pad, Kh = qa.shape
     N = qw.shape[0]
     K = 2 * Kh
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    st = _torch_stream(stream, qa.device)
     need = nvfp4_gemm_workspace_bytes(M, N, K)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=qa.device)
     nvfp4_gemm_ws(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, out.stride(0), workspace,
-                  need, stream)
+                  need, st)
     return out

@@ -282,6 +282,39 @@ def test_split_tail_after_full_waves(m):
     check(ref, (got_plain[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64), "plain rows")
 
 
+def test_convenience_gemm_on_a_non_current_stream(m):
+    """gemm(stream=s) with s not the current stream: the K-split workspace it
+    allocates belongs to s, so allocations and writes on the current stream
+    while s still runs (here behind a long matrix product) cannot take it over.
+    The output is bit-identical to the same call on the current stream."""
+    dev = device()
+    rng = np.random.default_rng(29)
+    M, N, K = 2560, 6656, 1024
+    need = m.nvfp4_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.02 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    args = (to_dev(qa), to_dev(sfa), to_dev(np.array([sa], np.float32)), M, to_dev(qw), to_dev(sfw),
+            to_dev(np.array([sw], np.float32)))
+    want = host_u16(m.gemm(*args))
+    side = torch.cuda.Stream(device=dev)
+    big = torch.randn((6144, 6144), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        busy = big @ big                      # keeps the side stream busy for a while
+    out = m.gemm(*args, stream=side)
+    for i in range(200):                      # reuse pressure on the current stream meanwhile
+        t = torch.empty(need, dtype=torch.uint8, device=dev)
+        t.fill_(0x7F)
+        torch.cuda._sleep(20000)
+        del t
+    torch.cuda.synchronize()
+    del busy
+    got = host_u16(out)
+    assert np.array_equal(got, want), first_mismatch(got, want)
+
+
 def test_split_tail_with_4byte_aligned_scales(m):
     """The K-split pieces with scale arrays that are only 4-byte aligned (the
     per-step scale path, offset to each piece's first K step)."""

@@ -501,27 +501,24 @@ def test_producer_canonical_37810_rows_byte_exact(m):
     assert s_g > 0
 
 
-def test_swiglu_canonical_37810_rows(m):
-    """The 37,810 x 2*14,336 FC2 producer: tensor scale over every row, QDATA
-    and SFA on all padding rows and on 2,048 sampled rows."""
+def test_fc1_producer_canonical_37810_rows_byte_exact(m):
+    """The FC1 projection's producer: the same 37,810 x 5,376 activation with
+    the FC1 shift/scale (their own seed), every row, both launch forms."""
+    w = synth.workload("fc1")
+    x = w.x()
+    rs, sh, sc = w.segments()
+    print(f"fc1 producer workload {x.shape}", flush=True)
+    s_g = check_modulate(m, x, rs, sh, sc)
+    assert s_g > 0
+
+
+def test_swiglu_canonical_37810_rows_byte_exact(m):
+    """The 37,810 x 2*14,336 FC2 SwiGLU producer: tensor scale, QDATA and SFA
+    of every row (padding included), in both launch forms."""
     w = synth.workload("fc2")
     gu = w.gate_up()
-    M = w.M
     print(f"swiglu workload {gu.shape}", flush=True)
-    gq, gs, gts, gamax = m.swiglu_quantize(to_dev_u16(gu))
-    torch.cuda.synchronize()
-    amax = _par.amax_merge(_par._map(lambda r: oracle.swiglu_amax_rows(gu, *r), _par._ranges(M, 64)))
-    s_g = oracle.tensor_scale(amax)
-    assert host(gamax)[0] == amax and host(gts)[0] == np.float32(s_g)
-    rows = np.unique(np.concatenate([synth.sample_rows(5, M, 2048, w.boundary_rows), np.arange(M, w.m_pad)]))
-    gq_h, gs_h = host(gq), host(gs)
-    for r0 in range(0, rows.size, 256):
-        rr = rows[r0:r0 + 256]
-        parts = _par._map(lambda r: oracle.swiglu_pack_rows(gu, s_g, r, r + 1), list(rr))
-        q = np.concatenate([p[0] for p in parts])
-        s = np.concatenate([p[1] for p in parts])
-        assert np.array_equal(gs_h[rr], s), first_mismatch(gs_h[rr], s)
-        assert np.array_equal(gq_h[rr], q), first_mismatch(gq_h[rr], q)
+    check_swiglu(m, gu)
 
 
 # Inputs past 4 GiB: byte offsets beyond 2^32, where the producers leave the

@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--two-pass", action="store_true",
                    help="run every producer as its two passes (absmax, pack: separate calls, per-pass times) instead of one call")
     p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    p.add_argument("--no-ring", action="store_true",
+                   help="skip the separately timed QKV projection through the packed-tile ring")
     p.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the step's outputs")
     p.add_argument("--no-standalone", action="store_true",
                    help="skip the standalone cold/warm producer timings (profiling runs)")
@@ -336,9 +338,65 @@ def main():
 
     if not args.no_attn_out:
         result["attn_out"] = attn_out_projection(nv, synth, dev, stream, args.steps)
+    if not args.no_ring:
+        result["ring"] = ring_projection(nv, x, seg_structs["qkv"][0], weights["qkv"], bufs["qkv"], M, M_pad, wq,
+                                         dev, stream, reps=max(5, args.steps))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, x_h, segs, gu_h, (wq, wf1, wf2))
     print(json.dumps(result), flush=True)
+
+
+def ring_projection(nv, x, seg, weight, b, M, M_pad, w, dev, stream, reps):
+    """The QKV projection through the packed-tile ring (nvfp4_modulate_gemm_ring)
+    timed next to the chained path (single-launch producer + GEMM) on the same
+    stream, alternating, after the step; not part of value."""
+    import numpy as np
+    import torch
+
+    qw, sfw, tw = weight
+    K, N = w.K, w.N
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    variants = {}
+    for chunk, slots in ((2048, 3), (2304, 3), (4096, 3)):
+        ring = torch.empty(slots * nv.nvfp4_ring_slot_bytes(chunk, K), dtype=torch.uint8, device=dev)
+        gws_bytes = nv.nvfp4_ring_gemm_workspace_bytes(M, chunk, N, K)
+        gws = torch.empty(max(gws_bytes, 16), dtype=torch.uint8, device=dev)
+        variants[f"ring_{chunk}x{slots}"] = (
+            lambda ring=ring, gws=gws, gws_bytes=gws_bytes, chunk=chunk, slots=slots: nv.nvfp4_modulate_gemm_ring(
+                x, M, K, K, seg, b["ws"], b["ts"], b["amax"], ring, slots, chunk, qw, sfw, tw, N, out, N, gws,
+                gws_bytes, stream))
+
+    def chained():
+        nv.nvfp4_modulate_quantize(x, M, K, K, seg, b["ws"], b["ts"], b["amax"], b["q"], b["s"], M_pad, stream)
+        nv.nvfp4_gemm_ws(b["q"], b["s"], b["ts"], M, M_pad, qw, sfw, tw, N, K, b["out"], N, b["gws"], b["gws_bytes"],
+                         stream)
+
+    runs = {"chained": chained, **variants}
+    times = {k: [] for k in runs}
+    for fn in runs.values():  # warm-up
+        fn()
+    stream.synchronize()
+    for _ in range(reps):
+        for k, fn in runs.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            times[k].append((e0, e1))
+    stream.synchronize()
+    ms = {k: float(np.median([a.elapsed_time(z) for a, z in v])) for k, v in times.items()}
+    full_rows = (M // 2304) * 2304  # rows of the full 2304-row chunks (no K-split tiles in either path there)
+    same = bool(torch.equal(out[:full_rows].view(torch.int16), b["out"][:full_rows].view(torch.int16)))
+    flop = 2.0 * M * N * K
+    return {
+        "workload": "QKV projection M=37810 K=5376 N=21504: pass 1 over all rows, then chunks packed into a ring of "
+                    "slots and multiplied (packs and odd/even chunk GEMMs on three streams); timed after the step, "
+                    "alternating with the chained path; not part of value",
+        "ms_p50": {k: round(v, 4) for k, v in ms.items()},
+        "TFLOPs": {k: round(flop / (v * 1e-3) / 1e12, 1) for k, v in ms.items()},
+        "vs_chained": {k: round(ms["chained"] / v, 4) for k, v in ms.items() if k != "chained"},
+        "outputs_equal_chained_full_chunks": same,
+    }
 
 
 def output_hashes(bufs):

@@ -286,6 +286,59 @@ nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, con
                                       int64_t ldr, uint16_t* out, int64_t ldo, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ---- Packed-tile ring ---------------------------------------------------
+ * "NVFP4 Streaming Design", P2 (N-group reuse): instead of materializing the
+ * whole packed activation, a bounded ring of packed row slots; one tensor
+ * scale from the full activation is reused by every chunk, each chunk of rows
+ * is packed into a slot and multiplied by the whole weight, and the slot is
+ * recycled.  The pages chose 2048-row chunks (18 full ones and a last one of
+ * 946 rows at 37,810 rows) and reported the ring slower than the
+ * materialized path at block level on their GPU; here it is an opt-in entry
+ * point with the same results as nvfp4_modulate_quantize followed by
+ * nvfp4_gemm_ws, so the two can be compared. */
+
+/* Bytes of one ring slot: chunk_rows rows of QDATA (K/2 bytes each) followed
+ * by chunk_rows rows of SFA (K/16 bytes each).  0 for an invalid argument
+ * (chunk_rows and K must be positive multiples of 64). */
+size_t nvfp4_ring_slot_bytes(int64_t chunk_rows, int64_t K);
+
+/* Bytes of GEMM workspace nvfp4_modulate_gemm_ring needs: two K-split
+ * workspaces (one per GEMM stream) for the larger of a full and the last
+ * chunk.  0 when no chunk's GEMM splits (or for an invalid argument). */
+size_t nvfp4_ring_gemm_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t N, int64_t K);
+
+/* Modulation producer and GEMM through a ring of `slots` packed slots:
+ *   1. pass 1 over all M rows of x [M, K]: *tensor_scale, *amax_out (may be
+ *      NULL), as nvfp4_modulate_absmax (same workspace rules);
+ *   2. for chunk c (rows [c*chunk_rows, min(M, (c+1)*chunk_rows))): pass 2 of
+ *      its rows into slot c % slots (rows past the chunk's last row up to the
+ *      next multiple of 64 are zero), then the GEMM of that slot against the
+ *      packed weight qw [N, K/2], sfw [N, K/16] with alpha = RN(*tensor_scale
+ *      * *w_scale), written to out rows [c*chunk_rows, ...) (bf16 [M, ldo]).
+ * The slot bytes of chunk c equal rows c*chunk_rows .. of the QDATA/SFA that
+ * nvfp4_modulate_quantize writes; the outputs satisfy nvfp4_gemm's contract
+ * and, when chunk_rows is a multiple of 256, equal nvfp4_gemm_ws's bit for bit
+ * except in tiles that either call computes as K-split pieces.
+ * Streams: pass 1 and the even chunks' GEMMs run on `stream`; the packs and
+ * the odd chunks' GEMMs on two streams the library creates once per device
+ * (default priority), ordered by events: a pack waits for the GEMM that last
+ * read its slot, a GEMM for its chunk's pack, and `stream` waits for all of it
+ * before its next work, so the call is stream-ordered for the caller.  No
+ * workgroup waits on another.  The ring (16-byte aligned, at least
+ * slots * nvfp4_ring_slot_bytes(chunk_rows, K) bytes) and gemm_workspace
+ * (nvfp4_ring_gemm_workspace_bytes) are caller-owned and must not be shared
+ * with calls that may overlap; calls on one device are enqueued one at a time
+ * (a host lock).
+ * Requirements: those of nvfp4_modulate_absmax, nvfp4_modulate_pack and
+ * nvfp4_gemm_ws; 1 <= slots <= 64; chunk_rows a multiple of 64 with
+ * chunk_rows * K/2 < 2^32. */
+nvfp4_status nvfp4_modulate_gemm_ring(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const nvfp4_segments* seg, void* workspace, float* tensor_scale,
+                                      float* amax_out, uint8_t* ring, int32_t slots, int64_t chunk_rows,
+                                      const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N,
+                                      uint16_t* out, int64_t ldo, void* gemm_workspace, size_t gemm_workspace_bytes,
+                                      void* stream);
+
 /* ---- Single-step entry points ------------------------------------------
  * Elementwise versions of single producer steps, running the very device
  * functions the producer kernels use, so that each step can be checked over

@@ -70,6 +70,10 @@ def _load():
         "nvfp4_gemm_ws": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, P, I64, P, ctypes.c_size_t, V]),
         "nvfp4_gemm_gate_residual": (I32, [P, P, P, I64, I64, P, P, P, I64, I64, GATES, P, I64, P, I64, P,
                                             ctypes.c_size_t, V]),
+        "nvfp4_ring_slot_bytes": (ctypes.c_size_t, [I64, I64]),
+        "nvfp4_ring_gemm_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64, I64]),
+        "nvfp4_modulate_gemm_ring": (I32, [P, I64, I64, I64, SEG, P, P, P, P, I32, I64, P, P, P, I64, P, I64, P,
+                                           ctypes.c_size_t, V]),
         "nvfp4_step_modulate": (I32, [P, P, P, P, I64, V]),
         "nvfp4_step_swiglu": (I32, [P, P, P, I64, V]),
         "nvfp4_step_block_scale": (I32, [P, P, P, I64, V]),
@@ -262,6 +266,23 @@ def nvfp4_gemm_gate_residual(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K,
                                         _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def nvfp4_ring_slot_bytes(chunk_rows, K):
+    return int(lib.nvfp4_ring_slot_bytes(chunk_rows, K))
+
+
+def nvfp4_ring_gemm_workspace_bytes(M, chunk_rows, N, K):
+    return int(lib.nvfp4_ring_gemm_workspace_bytes(M, chunk_rows, N, K))
+
+
+def nvfp4_modulate_gemm_ring(x, M, K, ldx, seg, ws, tensor_scale, amax_out, ring, slots, chunk_rows, qw, sfw,
+                             w_scale, N, out, ldo, gemm_workspace, gemm_workspace_bytes, stream=None):
+    _check("nvfp4_modulate_gemm_ring",
+           lib.nvfp4_modulate_gemm_ring(_ptr(x), M, K, ldx, ctypes.byref(seg), _ptr(ws), _ptr(tensor_scale),
+                                        _ptr(amax_out), _ptr(ring), slots, chunk_rows, _ptr(qw), _ptr(sfw),
+                                        _ptr(w_scale), N, _ptr(out), ldo, _ptr(gemm_workspace),
+                                        gemm_workspace_bytes, _stream(stream)))
+
+
 def nvfp4_step_modulate(x, scale, shift, y, n, stream=None):
     _check("nvfp4_step_modulate",
            lib.nvfp4_step_modulate(_ptr(x), _ptr(scale), _ptr(shift), _ptr(y), n, _stream(stream)))
@@ -394,3 +415,34 @@ def gemm(qa, sfa, a_scale, M: int, qw, sfw, w_scale, out: torch.Tensor | None = 
     nvfp4_gemm_ws(qa, sfa, a_scale, M, M_pad, qw, sfw, w_scale, N, K, out, out.stride(0), workspace,
                   need, st)
     return out
+
+
+def modulate_gemm_ring(x: torch.Tensor, row_start, shift: torch.Tensor, scale: torch.Tensor, qw, sfw, w_scale,
+                       chunk_rows: int = 2048, slots: int = 2, out: torch.Tensor | None = None, stream=None,
+                       ring: torch.Tensor | None = None):
+    """Producer + GEMM through the packed-tile ring: x [M, K] bf16 -> out [M, N]
+    bf16; returns (out, tensor_scale f32[1], amax f32[1], ring).  The ring
+    (slots x nvfp4_ring_slot_bytes(chunk_rows, K) bytes) and the GEMM
+    workspace are allocated on the launch stream unless a ring is given."""
+    _bits16(x)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    N = qw.shape[0]
+    seg, keep = make_segments(row_start, shift, scale)
+    dev = x.device
+    st = _torch_stream(stream, dev)
+    slot = nvfp4_ring_slot_bytes(chunk_rows, K)
+    need = nvfp4_ring_gemm_workspace_bytes(M, chunk_rows, N, K)
+    with torch.cuda.stream(st):
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if ring is None or ring.numel() * ring.element_size() < slots * slot:
+            ring = torch.empty(slots * slot, dtype=torch.uint8, device=dev)
+        gws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    nvfp4_modulate_gemm_ring(x, M, K, x.stride(0), seg, workspace(dev, st), ts, amax, ring, slots, chunk_rows, qw,
+                             sfw, w_scale, N, out, out.stride(0), gws, need, st)
+    del keep
+    return out, ts, amax, ring

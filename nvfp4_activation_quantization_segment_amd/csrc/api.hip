@@ -60,6 +60,8 @@ constexpr int kAbsmaxWgs = 256;
 constexpr int kPackWgs = 1024;
 // The SwiGLU passes hold a 128 KB table in LDS: one workgroup per CU.
 constexpr int kSwigluPackWgs = 256;
+// The ring's chunk packs run in the gaps the GEMMs leave: few, long workgroups.
+constexpr int kRingPackWgs = 256;
 
 nvfp4_status check_segments(const nvfp4_segments* seg, int64_t M, int64_t D, SegParams* out) {
     if (!seg || !seg->row_start || !seg->shift || !seg->scale) return NVFP4_ERR_INVALID_ARGUMENT;
@@ -450,6 +452,180 @@ nvfp4_status nvfp4_gemm_gate_residual(const uint8_t* qa, const uint8_t* sfa, con
     a.residual = residual;
     a.ldr = ldr;
     return run_gemm(a, M, M_pad, workspace, need > 0, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// Packed-tile ring ("NVFP4 Streaming Design", P2: N-group reuse through a
+// bounded ring of packed activation slots, one full-activation scale reused
+// by every chunk).  Host orchestration over three streams: the caller's
+// stream runs pass 1 and the even chunks' GEMMs, one internal stream the
+// chunk packs, another the odd chunks' GEMMs.  Events order every slot's
+// reuse (a pack waits for the GEMM that last read its slot) and every GEMM
+// (it waits for its chunk's pack), so no workgroup ever waits on another.
+// Two GEMM streams let one chunk's GEMM fill the CUs that the previous
+// chunk's last wave of tiles leaves idle, and the packs run in those gaps.
+// ---------------------------------------------------------------------------
+constexpr int kMaxRingSlots = 64;
+
+struct RingState {
+    bool ready = false;
+    hipStream_t pack = nullptr, gemm_odd = nullptr;
+    hipEvent_t start = nullptr, odd_done = nullptr;
+    hipEvent_t packed[kMaxRingSlots] = {};
+    hipEvent_t consumed[kMaxRingSlots] = {};
+};
+static RingState g_ring[kMaxDevices];
+static std::mutex g_ring_mu[kMaxDevices];
+
+static nvfp4_status ring_state(int dev, RingState** out) {
+    RingState& r = g_ring[dev];
+    if (!r.ready) {
+        hipError_t e;
+        if ((e = hipStreamCreateWithFlags(&r.pack, hipStreamNonBlocking)) != hipSuccess) return hip_status(e);
+        if ((e = hipStreamCreateWithFlags(&r.gemm_odd, hipStreamNonBlocking)) != hipSuccess) return hip_status(e);
+        if ((e = hipEventCreateWithFlags(&r.start, hipEventDisableTiming)) != hipSuccess) return hip_status(e);
+        if ((e = hipEventCreateWithFlags(&r.odd_done, hipEventDisableTiming)) != hipSuccess) return hip_status(e);
+        for (int i = 0; i < kMaxRingSlots; ++i) {
+            if ((e = hipEventCreateWithFlags(&r.packed[i], hipEventDisableTiming)) != hipSuccess) return hip_status(e);
+            if ((e = hipEventCreateWithFlags(&r.consumed[i], hipEventDisableTiming)) != hipSuccess)
+                return hip_status(e);
+        }
+        r.ready = true;
+    }
+    *out = &r;
+    return NVFP4_OK;
+}
+
+// Rows of every chunk's slot: chunk_rows (a multiple of 64), so that the last,
+// shorter chunk's padding rows fit too.
+static size_t ring_slot_bytes(int64_t chunk_rows, int64_t K) {
+    return (size_t)chunk_rows * (size_t)(K / 2 + K / 16);
+}
+
+// K-split workspace of one chunk GEMM (the largest of a full and the last
+// chunk), for each of the two GEMM streams.
+static size_t ring_gemm_ws_half(int64_t M, int64_t chunk_rows, int64_t N, int64_t K) {
+    const int64_t full = M < chunk_rows ? M : chunk_rows;
+    const int64_t last = M - (M - 1) / chunk_rows * chunk_rows;
+    const size_t a = gemm_workspace(full, N, K), b = gemm_workspace(last, N, K);
+    const size_t w = a > b ? a : b;
+    return (w + 255) / 256 * 256;
+}
+
+// The segment table restricted to rows [r0, r1), rebased to row 0.
+static void chunk_segments(const SegParams& sp, int64_t r0, int64_t r1, SegParams* out) {
+    memset(out, 0, sizeof(*out));
+    int s0 = 0;
+    while (sp.row_start[s0 + 1] <= r0) ++s0;
+    int n = 0;
+    out->row_start[0] = 0;
+    for (int s = s0; s < sp.count && sp.row_start[s] < r1; ++s) {
+        const int64_t hi = sp.row_start[s + 1] < r1 ? sp.row_start[s + 1] : r1;
+        out->row_start[++n] = hi - r0;
+    }
+    out->count = n;
+    out->shift = sp.shift + (int64_t)s0 * sp.ld;
+    out->scale = sp.scale + (int64_t)s0 * sp.ld;
+    out->ld = sp.ld;
+}
+
+static nvfp4_status ring_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const SegParams& sp,
+                             void* workspace, float* tensor_scale, float* amax_out, uint8_t* ring, int slots,
+                             int64_t chunk_rows, const GemmArgs& ga, uint8_t* gemm_ws, size_t ws_half,
+                             hipStream_t s, RingState& rs) {
+    nvfp4_status st;
+    // pass 1 over every row: one tensor scale for all chunks
+    const RowGeo g1 = row_geo(M, M, K, ldx, kAbsmaxWgs, 0, 8);
+    if ((st = hip_status(launch_modulate_absmax(x, g1, sp, (uint32_t*)workspace, tensor_scale, amax_out, false,
+                                                s))) != NVFP4_OK)
+        return st;
+    if ((st = hip_status(hipEventRecord(rs.start, s))) != NVFP4_OK) return st;
+    if ((st = hip_status(hipStreamWaitEvent(rs.pack, rs.start, 0))) != NVFP4_OK) return st;
+    if ((st = hip_status(hipStreamWaitEvent(rs.gemm_odd, rs.start, 0))) != NVFP4_OK) return st;
+    const size_t slot_bytes = ring_slot_bytes(chunk_rows, K);
+    const int64_t chunks = (M + chunk_rows - 1) / chunk_rows;
+    for (int64_t c = 0; c < chunks; ++c) {
+        const int slot = (int)(c % slots);
+        const int64_t r0 = c * chunk_rows;
+        const int64_t rows = M - r0 < chunk_rows ? M - r0 : chunk_rows;
+        const int64_t rows_pad = pad64(rows);
+        uint8_t* q = ring + (size_t)slot * slot_bytes;
+        uint8_t* sf = q + (size_t)chunk_rows * (K / 2);
+        // pack chunk c into its slot once the GEMM that last read the slot is done
+        if (c >= slots && (st = hip_status(hipStreamWaitEvent(rs.pack, rs.consumed[slot], 0))) != NVFP4_OK)
+            return st;
+        SegParams cs;
+        chunk_segments(sp, r0, r0 + rows, &cs);
+        const RowGeo g2 = row_geo(rows, rows_pad, K, ldx, kRingPackWgs, 1, 16);
+        if ((st = hip_status(launch_modulate_pack(x + r0 * ldx, g2, cs, tensor_scale, q, sf, false, rs.pack))) !=
+            NVFP4_OK)
+            return st;
+        if ((st = hip_status(hipEventRecord(rs.packed[slot], rs.pack))) != NVFP4_OK) return st;
+        // the chunk's GEMM on the even or the odd GEMM stream
+        const hipStream_t gs = (c & 1) ? rs.gemm_odd : s;
+        if ((st = hip_status(hipStreamWaitEvent(gs, rs.packed[slot], 0))) != NVFP4_OK) return st;
+        GemmArgs a = ga;
+        a.qa = q;
+        a.sfa = sf;
+        a.out = ga.out + r0 * ga.ldo;
+        void* ws = gemm_ws ? gemm_ws + ((c & 1) ? ws_half : 0) : nullptr;
+        if ((st = run_gemm(a, rows, rows_pad, ws, ws_half > 0, gs)) != NVFP4_OK) return st;
+        if ((st = hip_status(hipEventRecord(rs.consumed[slot], gs))) != NVFP4_OK) return st;
+    }
+    // the caller's stream continues after the odd GEMMs (whose packs precede them)
+    if ((st = hip_status(hipEventRecord(rs.odd_done, rs.gemm_odd))) != NVFP4_OK) return st;
+    return hip_status(hipStreamWaitEvent(s, rs.odd_done, 0));
+}
+
+size_t nvfp4_ring_slot_bytes(int64_t chunk_rows, int64_t K) {
+    if (chunk_rows <= 0 || chunk_rows % 64 != 0 || K <= 0 || K % 64 != 0) return 0;
+    return ring_slot_bytes(chunk_rows, K);
+}
+
+size_t nvfp4_ring_gemm_workspace_bytes(int64_t M, int64_t chunk_rows, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0 || chunk_rows <= 0 || chunk_rows % 64 != 0 ||
+        chunk_rows >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31) ||
+        gemm_chunk_rows(K) == 0 || chunk_rows > gemm_chunk_rows(K))
+        return 0;
+    return 2 * ring_gemm_ws_half(M, chunk_rows, N, K);
+}
+
+nvfp4_status nvfp4_modulate_gemm_ring(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const nvfp4_segments* seg, void* workspace, float* tensor_scale,
+                                      float* amax_out, uint8_t* ring, int32_t slots, int64_t chunk_rows,
+                                      const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N,
+                                      uint16_t* out, int64_t ldo, void* gemm_workspace, size_t gemm_workspace_bytes,
+                                      void* stream) {
+    nvfp4_status st = check_rows(x, M, K, ldx);
+    if (st != NVFP4_OK) return st;
+    SegParams sp;
+    if ((st = check_segments(seg, M, K, &sp)) != NVFP4_OK) return st;
+    if (!workspace || !tensor_scale || !ring) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, 4) || !aligned(tensor_scale, 4) || !aligned(amax_out, 4) || !aligned(ring, 16))
+        return NVFP4_ERR_ALIGNMENT;
+    if (slots < 1 || slots > kMaxRingSlots || chunk_rows <= 0) return NVFP4_ERR_INVALID_ARGUMENT;
+    if (chunk_rows % 64 != 0 || K % 64 != 0) return NVFP4_ERR_SHAPE;
+    // one chunk's packed rows and its GEMM use 32-bit offsets
+    if (chunk_rows > gemm_chunk_rows(K) || chunk_rows * (K / 2) >= ((int64_t)1 << 32)) return NVFP4_ERR_SHAPE;
+    GemmArgs ga;
+    // the activation arguments are per chunk; validate the rest with the first slot
+    if ((st = gemm_args(ring, ring + chunk_rows * (K / 2), tensor_scale, chunk_rows < M ? chunk_rows : M,
+                        chunk_rows, qw, sfw, w_scale, N, K, out, ldo, &ga)) != NVFP4_OK)
+        return st;
+    const size_t half = ring_gemm_ws_half(M, chunk_rows, N, K);
+    if (half > 0) {
+        if (!gemm_workspace || gemm_workspace_bytes < 2 * half) return NVFP4_ERR_INVALID_ARGUMENT;
+        if (!aligned(gemm_workspace, 16)) return NVFP4_ERR_ALIGNMENT;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lock(g_ring_mu[dev]);
+    RingState* rs = nullptr;
+    if ((st = ring_state(dev, &rs)) != NVFP4_OK) return st;
+    return ring_run(x, M, K, ldx, sp, workspace, tensor_scale, amax_out, ring, slots, chunk_rows, ga,
+                    (uint8_t*)gemm_workspace, half, (hipStream_t)stream, *rs);
 }
 
 static nvfp4_status step(int which, const void* a, const void* b, const void* c, void* out, int64_t n,

@@ -14,6 +14,8 @@
 // than 1024), so each row is read with contiguous 16-byte loads and the
 // per-column bf16(scale+1) and shift stay in registers.  Workgroups take rows
 // grid-stride, so the rows in flight form one compact window of the tensor.
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "internal.h"
 
@@ -153,10 +155,28 @@ __device__ __forceinline__ int seg_advance(const SegParams& seg, int64_t r, int 
 // the workgroups resident at any moment read one compact window of the tensor
 // that sweeps through it, which is what the memory system streams best.
 // PLAIN: y = x (the plain quantizer; seg is not read).
-template <bool PLAIN>
-__global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* __restrict__ x, RowGeo g,
-                                                               SegParams seg, uint32_t* ws,
-                                                               float* tensor_scale, float* amax_out) {
+// Running maximum of the magnitudes of the unrounded modulation sums of 8
+// columns (NaN once any is NaN); see mod16_max.
+__device__ __forceinline__ float mod8_max(const uint4& xv, const ColParams& cp, float m) {
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float sa = round_bf16(bf16_lo(xw[j]) * cp.s1[2 * j]) + cp.sh[2 * j];
+        const float sb = round_bf16(bf16_hi(xw[j]) * cp.s1[2 * j + 1]) + cp.sh[2 * j + 1];
+        m = __builtin_elementwise_maximum(
+            m, __builtin_elementwise_maximum(__builtin_fabsf(sa), __builtin_fabsf(sb)));
+    }
+    return m;
+}
+
+// Pass 1 of the modulation producer (and of the plain quantizer).  EXACT: the
+// maximum of the rounded y's bf16 magnitude bits; otherwise the maximum of the
+// unrounded sums, whose bf16 rounding is the same value (the kernel reruns the
+// exact form for a thread that met a NaN, so that the largest NaN bit pattern
+// is found as the exact form finds it).
+template <bool PLAIN, bool EXACT>
+__device__ __forceinline__ uint32_t modulate_absmax_rows(const uint16_t* __restrict__ x, const RowGeo& g,
+                                                         const SegParams& seg, float& mf) {
     const int64_t G = gridDim.x;
     uint32_t m2 = 0;
     for (int j = 0; j < g.J; ++j) {
@@ -167,45 +187,55 @@ __global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* _
         int64_t seg_end = seg.row_start[s + 1];  // rows only increase: one compare per row
         ColParams cp;
         if (!PLAIN) load_cols(seg, s, c, cp);
+        auto one = [&](const uint4& xv, int64_t rr) {
+            if constexpr (PLAIN) {
+                const uint32_t y[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
+            } else {
+                if (rr >= seg_end) {
+                    s = seg_advance(seg, rr, s);
+                    seg_end = seg.row_start[s + 1];
+                    load_cols(seg, s, c, cp);
+                }
+                if constexpr (EXACT) {
+                    uint32_t y[4];
+                    modulate8(xv, cp, y);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
+                } else {
+                    mf = mod8_max(xv, cp, mf);
+                }
+            }
+        };
         for (; r + 3 * G < g.M; r += 4 * G) {
             uint4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = ld16(x + (r + u * G) * g.ldx + 8 * c);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                uint32_t y[4];
-                if constexpr (PLAIN) {
-                    y[0] = v[u].x; y[1] = v[u].y; y[2] = v[u].z; y[3] = v[u].w;
-                } else {
-                    if (r + u * G >= seg_end) {
-                        s = seg_advance(seg, r + u * G, s);
-                        seg_end = seg.row_start[s + 1];
-                        load_cols(seg, s, c, cp);
-                    }
-                    modulate8(v[u], cp, y);
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
-            }
+            for (int u = 0; u < 4; ++u) one(v[u], r + u * G);
         }
-        for (; r < g.M; r += G) {
-            uint32_t y[4];
-            const uint4 xv = ld16(x + r * g.ldx + 8 * c);
-            if constexpr (PLAIN) {
-                y[0] = xv.x; y[1] = xv.y; y[2] = xv.z; y[3] = xv.w;
-            } else {
-                if (r >= seg_end) {
-                    s = seg_advance(seg, r, s);
-                    seg_end = seg.row_start[s + 1];
-                    load_cols(seg, s, c, cp);
-                }
-                modulate8(xv, cp, y);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
-        }
+        for (; r < g.M; r += G) one(ld16(x + r * g.ldx + 8 * c), r);
     }
-    reduce_and_finish(fold_max(m2), ws, tensor_scale, amax_out);
+    return m2;
+}
+
+template <bool PLAIN>
+__global__ __launch_bounds__(1024) void modulate_absmax_kernel(const uint16_t* __restrict__ x, RowGeo g,
+                                                               SegParams seg, uint32_t* ws,
+                                                               float* tensor_scale, float* amax_out) {
+    float mf = 0.0f;
+    uint32_t m;
+    if constexpr (PLAIN) {
+        m = fold_max(modulate_absmax_rows<true, true>(x, g, seg, mf));
+    } else {
+        modulate_absmax_rows<false, false>(x, g, seg, mf);
+        if (mf == mf)
+            m = __float_as_uint(round_bf16(mf)) >> 16;
+        else
+            m = fold_max(modulate_absmax_rows<false, true>(x, g, seg, mf));
+    }
+    reduce_and_finish(m, ws, tensor_scale, amax_out);
 }
 
 // Pass 2: one thread per 16-value block (two 16-byte loads per row), so the
@@ -675,6 +705,25 @@ __device__ __forceinline__ float max_abs2(float m, float a, float b) {
     return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)));
 }
 
+// Running maximum of the magnitudes of the unrounded modulation sums of 16
+// columns (NaN once any sum is NaN).  bf16 rounding is monotone and odd, so
+// the bf16 rounding of this maximum is the largest |y| of those columns: pass
+// 1 needs no rounded y for rows it does not keep (two VALU operations fewer
+// per pair of columns than modulating and taking the maximum of the bits).
+__device__ __forceinline__ float mod16_max(const uint4& a, const uint4& c, const ColParams& p0, const ColParams& p1,
+                                           float m) {
+    const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const ColParams& p = j < 4 ? p0 : p1;
+        const int k = 2 * (j & 3);
+        const float sa = round_bf16(bf16_lo(xw[j]) * p.s1[k]) + p.sh[k];
+        const float sb = round_bf16(bf16_hi(xw[j]) * p.s1[k + 1]) + p.sh[k + 1];
+        m = max_abs2(m, sa, sb);
+    }
+    return m;
+}
+
 // y of 16 columns as binary32 values (each exactly a bf16) and the largest
 // magnitude of the unrounded sums (NaN if any sum is NaN).  Rounding to bf16
 // is monotone and odd, so the bf16 rounding of that maximum is the block's
@@ -931,7 +980,6 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
     uint32_t m2 = 0;
     uint32_t hy[HR][8];
-    int t = 0;
     int s = 0, seg_hi = 0;
     ColPk cp;
     if (on) {
@@ -959,11 +1007,16 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             hold_put(hold, tl - hs.ns, y);
         }
     }
-    {
-        // streamed groups, two per iteration, with binary32 column parameters
-        // (short of VALU here, not of registers: the held groups come later)
+    // streamed groups, two per iteration, with binary32 column parameters
+    // (short of VALU here, not of registers: the held groups come later).
+    // EXACT: the maximum of the rounded y's bit patterns (the plain quantizer,
+    // and the rare rerun after a NaN); otherwise the maximum of the unrounded
+    // sums (mod16_max), whose bf16 rounding is the same value.
+    auto streamed = [&](auto exact) {
+        constexpr bool EXACT = decltype(exact)::value;
         ColParams c0, c1;
         int hi = 0, sc = 0;
+        float mf = 0.0f;
         if (!PLAIN && on) {
             sc = seg_find(seg, r_first < g.M ? r_first : 0, 0);
             load_cols(seg, sc, 2 * b, c0);
@@ -971,10 +1024,9 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             hi = (int)seg.row_start[sc + 1];
         }
         auto absmax = [&](const uint4& v0, const uint4& v1, int r) {
-            uint32_t y[8];
             if constexpr (PLAIN) {
-                y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
-                y[4] = v1.x; y[5] = v1.y; y[6] = v1.z; y[7] = v1.w;
+                const uint32_t y[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                max16(m2, y);
             } else {
                 if (r >= hi) {
                     sc = seg_find(seg, r, sc);
@@ -982,10 +1034,16 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                     load_cols(seg, sc, 2 * b, c0);
                     load_cols(seg, sc, 2 * b + 1, c1);
                 }
-                mod16_packed(v0, v1, c0, c1, y);
+                if constexpr (EXACT) {
+                    uint32_t y[8];
+                    mod16_packed(v0, v1, c0, c1, y);
+                    max16(m2, y);
+                } else {
+                    mf = mod16_max(v0, v1, c0, c1, mf);
+                }
             }
-            max16(m2, y);
         };
+        int t = 0;
         for (; t + 1 < hs.ns; t += 2) {
             if (on) {
                 const int r0 = r_first + t * gstride, r1 = r0 + gstride;
@@ -1000,6 +1058,16 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
             const uint32_t o0 = (uint32_t)(r_first + t * gstride) * xrow + xcol;
             absmax(ld16o(xb, o0), ld16o(xb, o0 + 16), r_first + t * gstride);
         }
+        return mf;
+    };
+    if constexpr (PLAIN) {
+        streamed(std::true_type{});
+    } else {
+        const float mf = streamed(std::false_type{});
+        if (mf == mf)
+            m2 = pk_max_u16(m2, __float_as_uint(round_bf16(mf)) >> 16);
+        else
+            streamed(std::true_type{});  // a NaN: the largest NaN bit pattern, exactly
     }
     if (on) {
         // register-held groups: all loads first, then y in place of x

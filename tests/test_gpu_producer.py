@@ -149,6 +149,45 @@ def test_tiny_global_maximum_uses_exact_division(m):
     check_values(m, y)
 
 
+@pytest.mark.parametrize("where", ["streamed", "held", "both"])
+def test_nan_inputs_give_the_largest_nan_pattern(m, where):
+    """NaN in x ([12000, 5376], 256 workgroups: rows of a workgroup's first
+    groups are streamed in pass 1, the last ones held): the tensor maximum is
+    the largest bf16 magnitude bit pattern of the device's own y (from the
+    modulation step entry point on the same elements), in both launch forms,
+    and every block packs to the NaN scale code with zero codes, as in the
+    oracle.  Pass 1 takes the maximum of unrounded sums and reruns exactly
+    when it meets a NaN, which this checks."""
+    M, D = 12000, 5376
+    x = synth.normal_bf16(81, 0, (M, D), 1.0)
+    sh = synth.normal_bf16(81, 1, (2, D), 0.1)
+    sc = synth.normal_bf16(81, 2, (2, D), 0.1)
+    rs = [0, 7000, M]
+    if where in ("streamed", "both"):
+        x[1, 5] = 0x7FA1          # row 1: in workgroup 0's first (streamed) group
+        x[4, 77] = 0xFFD3
+    if where in ("held", "both"):
+        x[M - 1, 4000] = 0x7FC9   # the last row: a register-held group
+    seg_of = np.searchsorted(np.array(rs[1:]), np.arange(M), side="right")
+    dev = device()
+    y = torch.empty(M * D, dtype=torch.int16, device=dev)
+    m.nvfp4_step_modulate(to_dev_u16(x.ravel()), to_dev_u16(sc[seg_of].ravel()), to_dev_u16(sh[seg_of].ravel()), y,
+                          M * D)
+    torch.cuda.synchronize()
+    ymag = host(y).view(np.uint16) & 0x7FFF
+    want_bits = np.uint32(ymag.max()) << 16
+    assert (want_bits >> 16) > 0x7F80  # a NaN pattern
+    seg = oracle.Segments(rs, sh, sc)
+    _, oq, osf, _ = _par.modulate_quantize(x, seg, oracle.padded_rows(M))
+    for single in (False, True):
+        gs, gq, gsf, gamax = gpu_modulate(m, x, rs, sh, sc, single_pass=single)
+        path = "single launch" if single else "two passes"
+        assert np.float32(gamax).view(np.uint32) == want_bits, (path, hex(int(np.float32(gamax).view(np.uint32))))
+        assert np.isnan(gs), path
+        assert np.array_equal(gsf, osf) and (gsf[:M] == 0x7F).all(), path + ": SFA " + str(first_mismatch(gsf, osf))
+        assert np.array_equal(gq, oq) and not gq.any(), path
+
+
 def test_workspace_reuse_between_calls(m):
     """Calls in a row on one workspace, alternating the single launch and the
     two passes: each sees only its own tensor (the maxima differ).  The two

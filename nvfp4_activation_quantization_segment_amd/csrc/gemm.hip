@@ -37,6 +37,8 @@
 // several K ranges per tile (gemm_plan); the pieces store fp32 partial sums and
 // gemm_finalize_kernel adds them in K order before the alpha and the bf16
 // rounding.
+#include <type_traits>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -441,34 +443,52 @@ gemm_kernel(GemmArgs a, GemmPart p) {
                 }
             }
         } else if (n < a.N) {
-            // Residual epilogue: all 16 residual loads of the lane first (rows
-            // past M clamped to the last row, never stored), and one gate
-            // vector when the wave's 128 rows lie in one segment, so that the
-            // load latency is paid once rather than once per row.
+            // Residual epilogue: the lane's residual loads issued 8 rows at a
+            // time (rows past M clamped to the last row, never stored; 8
+            // rather than all 16, which would not fit the registers left and
+            // spilled), and one gate vector when the wave's 128 rows lie in
+            // one segment, so that the load latency is paid twice rather than
+            // once per row.
             const int wfirst = tm * kBM + wm * kWM;
             const int wlast = wfirst + kWM - 1 < a.M - 1 ? wfirst + kWM - 1 : a.M - 1;
             const uint16_t* g_first = gate_row(a, wfirst < a.M ? wfirst : a.M - 1);
             const bool one_gate = g_first == gate_row(a, wlast);
             const uint4 g_wave = *reinterpret_cast<const uint4*>(g_first + n);
-            uint4 res[kWM / 8];
+            // The choice of gate is a wave-uniform branch around the whole
+            // loop: a per-row select between g_wave and a load would become a
+            // load through a selected pointer, with g_wave put on the stack.
+            const auto rows = [&](auto one) {
+                constexpr int kBatch = 8;
 #pragma unroll
-            for (int it = 0; it < kWM / 8; ++it) {
-                const int m = m0 + 8 * it < a.M ? m0 + 8 * it : a.M - 1;
-                res[it] = *reinterpret_cast<const uint4*>(a.residual + (int64_t)m * a.ldr + n);
-            }
+                for (int b0 = 0; b0 < kWM / 8; b0 += kBatch) {
+                    uint4 res[kBatch];
 #pragma unroll
-            for (int it = 0; it < kWM / 8; ++it) {
-                const int m = m0 + 8 * it;
-                if (m < a.M) {
-                    uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * it + (lane >> 3)) * kRowB + (lane & 7) * 16);
-                    const uint4 g = one_gate ? g_wave : *reinterpret_cast<const uint4*>(gate_row(a, m) + n);
-                    v.x = gate_residual2(v.x, g.x, res[it].x);
-                    v.y = gate_residual2(v.y, g.y, res[it].y);
-                    v.z = gate_residual2(v.z, g.z, res[it].z);
-                    v.w = gate_residual2(v.w, g.w, res[it].w);
-                    store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
+                    for (int it = 0; it < kBatch; ++it) {
+                        const int m = m0 + 8 * (b0 + it) < a.M ? m0 + 8 * (b0 + it) : a.M - 1;
+                        res[it] = *reinterpret_cast<const uint4*>(a.residual + (int64_t)m * a.ldr + n);
+                    }
+#pragma unroll
+                    for (int it = 0; it < kBatch; ++it) {
+                        const int m = m0 + 8 * (b0 + it);
+                        if (m < a.M) {
+                            uint4 v = *reinterpret_cast<const uint4*>(wl + (8 * (b0 + it) + (lane >> 3)) * kRowB +
+                                                                      (lane & 7) * 16);
+                            const uint4 g = decltype(one)::value
+                                                ? g_wave
+                                                : *reinterpret_cast<const uint4*>(gate_row(a, m) + n);
+                            v.x = gate_residual2(v.x, g.x, res[it].x);
+                            v.y = gate_residual2(v.y, g.y, res[it].y);
+                            v.z = gate_residual2(v.z, g.z, res[it].z);
+                            v.w = gate_residual2(v.w, g.w, res[it].w);
+                            store_nt(reinterpret_cast<uint4*>(a.out + (int64_t)m * a.ldo + n), v);
+                        }
+                    }
                 }
-            }
+            };
+            if (one_gate)
+                rows(std::true_type{});
+            else
+                rows(std::false_type{});
         }
         return;
     }

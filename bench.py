@@ -45,7 +45,8 @@ def parse():
                    help="skip the separately timed attention-output projection")
     p.add_argument("--two-pass", action="store_true",
                    help="run every producer as its two passes (absmax, pack: separate calls, per-pass times) instead of one call")
-    p.add_argument("--cpu-rows", type=int, default=48, help="rows per projection in the CPU-baseline sample")
+    p.add_argument("--cpu-rows", type=int, default=16,
+                   help="checked rows per projection for the CPU-baseline GEMM (x 8 rows of the SwiGLU producer)")
     p.add_argument("--no-ring", action="store_true",
                    help="skip the separately timed QKV projection through the packed-tile ring")
     p.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the step's outputs")
@@ -535,47 +536,21 @@ def _oracle_weight(oracle, wt):
     return sw, np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
-def _oracle_sample(oracle, x_h, gu_h, works, weights, rows, threads):
-    """Times the oracle on the first `rows` rows of each projection: producer
-    (amax, then pack) and the FP64 GEMM reference for those rows and all N.
-    With threads > 1 the producer's rows and the GEMM's output columns (the
-    weight rows, which the oracle decodes once per call) are split into ranges
-    run on a thread pool (the oracle's C calls release the GIL); the maxima of
-    the row ranges are merged exactly.  Returns (flop, producer bytes,
-    producer s, GEMM s)."""
-    import concurrent.futures as cf
+def _pool_map(ex, fn, items):
+    return list(ex.map(fn, items)) if ex is not None else [fn(i) for i in items]
 
-    import numpy as np
 
-    ranges = [(a * rows // threads, (a + 1) * rows // threads) for a in range(threads)]
-    ranges = [r for r in ranges if r[1] > r[0]]
-    t_flop = t_bytes = t_prod = t_gemm = 0.0
-    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        for w in works:
-            sw, qw, sfw = weights[w.name]
-            t0 = time.perf_counter()
-            if w.kind == "modulate":
-                rs, sh, sc = w.segments()
-                seg = oracle.Segments(rs, sh, sc)
-                amaxes = list(ex.map(lambda r: oracle.modulate_amax_rows(x_h, seg, *r), ranges))
-                s_g = oracle.tensor_scale(_max_bits(amaxes))
-                parts = list(ex.map(lambda r: oracle.modulate_pack_rows(x_h, seg, s_g, *r), ranges))
-                t_bytes += 2 * rows * w.K * 2 + rows * (w.K // 2 + w.K // 16)
-            else:
-                amaxes = list(ex.map(lambda r: oracle.swiglu_amax_rows(gu_h, *r), ranges))
-                s_g = oracle.tensor_scale(_max_bits(amaxes))
-                parts = list(ex.map(lambda r: oracle.swiglu_pack_rows(gu_h, s_g, *r), ranges))
-                t_bytes += 2 * rows * 2 * w.K * 2 + rows * (w.K // 2 + w.K // 16)
-            qa = np.concatenate([p[0] for p in parts])
-            sfa = np.concatenate([p[1] for p in parts])
-            t_prod += time.perf_counter() - t0
-            t0 = time.perf_counter()
-            cols = [(a * w.N // threads, (a + 1) * w.N // threads) for a in range(threads)]
-            list(ex.map(lambda c: oracle.gemm_rows(qa, sfa, s_g, qw[c[0]:c[1]], sfw[c[0]:c[1]], sw, np.arange(rows)),
-                        [c for c in cols if c[1] > c[0]]))
-            t_gemm += time.perf_counter() - t0
-            t_flop += 2.0 * rows * w.N * w.K
-    return t_flop, t_bytes, t_prod, t_gemm
+def _ranges(n, parts):
+    return [r for r in ((a * n // parts, (a + 1) * n // parts) for a in range(parts)) if r[1] > r[0]]
+
+
+def _oracle_modulation_producer(oracle, x_h, seg, M, M_pad, ex, parts):
+    """The whole modulation producer through the oracle: pass 1 over every row,
+    then pass 2 over every padded row (row ranges; maxima merged exactly)."""
+    s_g = oracle.tensor_scale(_max_bits(_pool_map(ex, lambda r: oracle.modulate_amax_rows(x_h, seg, *r),
+                                                  _ranges(M, parts))))
+    _pool_map(ex, lambda r: oracle.modulate_pack_rows(x_h, seg, s_g, *r), _ranges(M_pad, parts))
+    return s_g
 
 
 def _max_bits(vals):
@@ -588,35 +563,110 @@ def _max_bits(vals):
 
 
 def cpu_baseline(args, x_h, segs, gu_h, works):
-    """The oracle as it stands, timed on a bounded sample of the same step: for
-    each projection, the producer (both passes) over its first `cpu_rows` rows
-    and the FP64 GEMM reference for those rows and all N.  `value` is the
-    oracle single-threaded; `all_cores` the same sample over the host's cores.
-    Weight prepacking is not part of the step and is not timed."""
+    """The oracle as it stands, timed in the same run on this host.
+
+    - The whole producer of the 37,810 x 5,376 modulation workload (pass 1 over
+      every row, pass 2 over every padded row), once single-threaded and once
+      on all host cores (row ranges on a thread pool, maxima merged exactly).
+    - The SwiGLU producer on its first `cpu_rows` * 8 rows (single-threaded),
+      extrapolated to all rows.
+    - The FP64 GEMM reference on `cpu_rows` sampled rows of each projection
+      with all N (single-threaded), as seconds per row, extrapolated to all
+      37,810 rows.
+    `value` is the whole step at the oracle's single-threaded rates: GEMM flop
+    of the three projections / (measured modulation producer x 2 + the
+    extrapolated SwiGLU producer and GEMMs); `extrapolated` says which parts are
+    extrapolated.  Weight prepacking is not part of the step and is not timed."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
     import oracle
 
-    rows = args.cpu_rows
     oracle.lib()
-    weights = {}
-    for w in works:
-        weights[w.name] = _oracle_weight(oracle, w.weight())
-    flop, nbytes, t_prod, t_gemm = _oracle_sample(oracle, x_h, gu_h, works, weights, rows, 1)
-    total = t_prod + t_gemm
+    rows = args.cpu_rows
     cores = len(os.sched_getaffinity(0))
-    flop_n, _, tp_n, tg_n = _oracle_sample(oracle, x_h, gu_h, works, weights, rows, cores)
+    wq = works[0]
+    M, M_pad, K = wq.M, wq.m_pad, wq.K
+    rs, sh, sc = wq.segments()
+    seg = oracle.Segments(rs, sh, sc)
+    mod_bytes = 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
+
+    t0 = time.perf_counter()
+    _oracle_modulation_producer(oracle, x_h, seg, M, M_pad, None, 1)
+    t_mod1 = time.perf_counter() - t0
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        _oracle_modulation_producer(oracle, x_h, seg, M, M_pad, ex, 4 * cores)
+        t_modn = time.perf_counter() - t0
+
+    # SwiGLU producer on a row prefix, single-threaded
+    w2 = works[2]
+    sr = min(M, 8 * rows)
+    t0 = time.perf_counter()
+    a = oracle.swiglu_amax_rows(gu_h, 0, sr)
+    oracle.swiglu_pack_rows(gu_h, oracle.tensor_scale(a), 0, sr)
+    t_sw_rows = time.perf_counter() - t0
+    t_sw = t_sw_rows * M_pad / sr
+
+    # GEMM reference per checked row, single-threaded, on oracle-packed operands
+    gemm = {}
+    t_gemm_total = 0.0
+    flop_total = 0.0
+    for w in works:
+        # untimed preparation on the thread pool: oracle weight bytes, the
+        # activation's tensor scale and the checked rows' packed bytes
+        wts = w.weight()
+        sw, qw, sfw = _oracle_weight(oracle, wts)
+        del wts
+        chk = w.check_rows(rows)
+        with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+            if w.kind == "modulate":
+                rs_w, sh_w, sc_w = w.segments()
+                seg_w = oracle.Segments(rs_w, sh_w, sc_w)
+                s_a = oracle.tensor_scale(_max_bits(_pool_map(
+                    ex, lambda r: oracle.modulate_amax_rows(x_h, seg_w, *r), _ranges(M, 4 * cores))))
+                packed = [oracle.modulate_pack_rows(x_h, seg_w, s_a, int(r), int(r) + 1) for r in chk]
+            else:
+                s_a = oracle.tensor_scale(_max_bits(_pool_map(
+                    ex, lambda r: oracle.swiglu_amax_rows(gu_h, *r), _ranges(M, 4 * cores))))
+                packed = [oracle.swiglu_pack_rows(gu_h, s_a, int(r), int(r) + 1) for r in chk]
+        qa = np.concatenate([p[0] for p in packed])
+        sfa = np.concatenate([p[1] for p in packed])
+        # the reference decodes the whole weight once per call: timed alone
+        # (no rows), then with the checked rows; the difference per row
+        # scales to all rows
+        t0 = time.perf_counter()
+        oracle.gemm_rows(qa, sfa, s_a, qw, sfw, sw, np.arange(0))
+        t_dec = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.gemm_rows(qa, sfa, s_a, qw, sfw, sw, np.arange(chk.size))
+        t = time.perf_counter() - t0
+        per_row = max(t - t_dec, 1e-9) / chk.size
+        gemm[w.name] = {"rows_timed": int(chk.size), "s_weight_decode": round(t_dec, 3),
+                        "s_per_row": round(per_row, 4), "GFLOPs_per_row": round(2.0 * w.N * w.K / per_row / 1e9, 3),
+                        "extrapolated_s_all_rows": round(t_dec + per_row * M, 1)}
+        t_gemm_total += t_dec + per_row * M
+        flop_total += 2.0 * M * w.N * w.K
+    step_s = 2 * t_mod1 + t_sw + t_gemm_total
     return {
-        "value": round(flop / total / 1e12, 6),
+        "value": round(flop_total / step_s / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {rows} rows of each of QKV, FC1, FC2: producer (amax + pack over those rows) and FP64 "
-                  f"GEMM reference for all N; {total:.1f} s single-threaded",
-        "producer_GBps": round(nbytes / t_prod / 1e9, 4),
-        "gemm_TFLOPs": round(flop / t_gemm / 1e12, 6),
+        "sample": (f"whole 37,810 x 5,376 modulation producer measured ({t_mod1:.1f} s, 1 thread), counted for QKV "
+                   f"and FC1; SwiGLU producer timed on {sr} rows and FP64 GEMM reference on {rows} checked rows per "
+                   f"projection (all N), both extrapolated to 37,810 rows"),
+        "extrapolated": ["swiglu producer", "gemm"],
+        "step_s_extrapolated": round(step_s, 1),
+        "producer_full": {"workload": "modulation producer [37810, 5376], both passes, every row",
+                          "bytes": mod_bytes,
+                          "one_core": {"s": round(t_mod1, 2), "GBps": round(mod_bytes / t_mod1 / 1e9, 4)},
+                          "all_cores": {"cores": cores, "s": round(t_modn, 2),
+                                        "GBps": round(mod_bytes / t_modn / 1e9, 4)}},
+        "swiglu_producer": {"rows_timed": sr, "s": round(t_sw_rows, 2), "extrapolated_s_all_rows": round(t_sw, 1)},
+        "gemm": gemm,
         "host_cores_available": cores,
-        "all_cores": {"value": round(flop_n / (tp_n + tg_n) / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-                      "kind": "oracle on a thread pool (producer rows, GEMM output columns)",
-                      "seconds": round(tp_n + tg_n, 2)},
     }
 
 

@@ -101,6 +101,15 @@ int64_t nvfp4_padded_rows(int64_t m);
  * calls that may overlap. */
 size_t nvfp4_absmax_workspace_bytes(void);
 
+/* Byte offset, within that workspace, of a uint32 count of the single
+ * launches on it whose grid-barrier wait passed its bound (each such launch
+ * adds one, from the device).  The library never resets it; zeroing the
+ * workspace does.  A caller checks for timed-out launches without a host
+ * synchronization by copying these 4 bytes asynchronously, or by reading them
+ * in a later kernel on the same stream.  nvfp4_modulate_quantize_noalloc keeps
+ * no such count (it clears its words on every call). */
+#define NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET 192
+
 /* Sets the bound on the single launches' grid-barrier wait, in microseconds
  * (default 1,000,000), for launches enqueued from then on; returns the
  * previous bound.  A launch whose wait passes the bound completes with a NaN
@@ -154,7 +163,9 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
  * its own barrier), so concurrent launches complete; the workgroups that
  * start late find the barrier passed.  A wait past the bound of
  * nvfp4_set_barrier_timeout_us (1 s by default) gives a NaN tensor scale and
- * amax, scale code 0x7F and zero codes in every block, for that call only.
+ * amax, scale code 0x7F and zero codes in every block, for that call only,
+ * and adds one to the workspace's timeout count
+ * (NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET).
  * Calls that can overlap in time must use different workspaces.  When
  * D > 16384, or x spans 4 GiB or more, it enqueues the two passes instead.
  * Same requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack

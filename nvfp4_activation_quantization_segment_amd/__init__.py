@@ -164,6 +164,17 @@ def workspace(device=None, stream=None) -> torch.Tensor:
     return ws
 
 
+WORKSPACE_TIMEOUT_COUNT_OFFSET = 192  # NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET
+
+
+def workspace_timeouts(ws: torch.Tensor) -> int:
+    """The workspace's count of single launches whose grid-barrier wait passed
+    its bound (synchronizes with the workspace's stream to read it; a caller
+    that must not synchronize copies the 4 bytes asynchronously instead)."""
+    o = WORKSPACE_TIMEOUT_COUNT_OFFSET
+    return int(ws[o:o + 4].view(torch.int32).item())
+
+
 def set_barrier_timeout_us(microseconds: int) -> int:
     """Bound on the single launches' grid-barrier wait (default 1 s); returns
     the previous bound.  0 makes every single launch give up at once."""

@@ -487,6 +487,10 @@ __device__ __forceinline__ int seg_find(const SegParams& seg, int64_t r, int s) 
 // between the workgroup barrier after the write and the one before the next
 // write, so all waves take the same branch and meet the same barriers.
 constexpr int kResultQword = 16;                        // 64-bit word index (byte 128)
+constexpr int kTimeoutCountWord = NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET / 4;  // 32-bit word (byte 192)
+static_assert(NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET % 4 == 0 && NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET >= 136 &&
+                  NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET + 4 <= 256,
+              "the count lies in the header, clear of the maximum, counter and result words");
 constexpr int kSlotQword = 32;                          // workgroup 0's arrival word (byte 256)
 constexpr int kClaimQword = kSlotQword + kMaxGridSlots;  // workgroup 0's claim word
 constexpr uint32_t kPublished = 0x10000u, kAbandoned = 0x20000u;
@@ -519,12 +523,17 @@ __device__ __forceinline__ uint32_t outcome_bits(uint64_t r) {
 }
 
 // Settles the result word of tag `tag`: installs `want` unless a word of this
-// tag is already there; returns the word that holds.
-__device__ __forceinline__ uint64_t settle(uint64_t* res, uint64_t tag, uint64_t want) {
+// tag is already there; returns the word that holds, and in `installed`
+// whether this call put it there (one call per launch does).
+__device__ __forceinline__ uint64_t settle(uint64_t* res, uint64_t tag, uint64_t want, bool& installed) {
+    installed = false;
     uint64_t cur = load_dev64(res);
     while (tag_of(cur) != tag) {
         const uint64_t found = cas_dev64(res, cur, want);
-        if (found == cur) return want;
+        if (found == cur) {
+            installed = true;
+            return want;
+        }
         cur = found;
     }
     return cur;
@@ -590,7 +599,8 @@ __device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, const BarrierAr
             if (__syncthreads_and(next >= G)) {
                 const uint32_t all = workgroup_max(mine, red);
                 if (threadIdx.x == 0) {
-                    const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kPublished | all));
+                    bool installed;
+                    const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kPublished | all), installed);
                     write_scale(outcome_bits(r), tensor_scale, amax_out);
                     s_result = outcome_bits(r);
                 }
@@ -604,7 +614,11 @@ __device__ uint32_t grid_max_barrier(uint32_t m16, uint32_t* ws, const BarrierAr
             s_help = -1;
             s_cand = G;
             if (ba.wait_ticks == 0 || el > ba.wait_ticks) {
-                const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kAbandoned));
+                bool installed;
+                const uint64_t r = settle(&q[kResultQword], tag, tagged(tag, kAbandoned), installed);
+                // the one workgroup that abandoned this launch's barrier counts it
+                if (installed)
+                    __hip_atomic_fetch_add(ws + kTimeoutCountWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 write_scale(outcome_bits(r), tensor_scale, amax_out);
                 s_result = outcome_bits(r);
                 s_done = 1;

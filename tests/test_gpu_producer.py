@@ -242,9 +242,10 @@ def test_barrier_timeout_gives_nan_for_that_call_only(m):
                 torch.full((m_pad, D // 2), 0x55, dtype=torch.uint8, device=dev),
                 torch.full((m_pad, D // 16), 0x55, dtype=torch.uint8, device=dev))
 
+    assert m.workspace_timeouts(ws) == 0
     previous = m.set_barrier_timeout_us(0)
     try:
-        for kind in ("modulate", "swiglu", "modulate"):
+        for i, kind in enumerate(("modulate", "swiglu", "modulate")):
             ts, a, q, s = outputs()
             if kind == "modulate":
                 m.nvfp4_modulate_quantize(to_dev_u16(x), M, D, D, seg, ws, ts, a, q, s, m_pad)
@@ -256,6 +257,7 @@ def test_barrier_timeout_gives_nan_for_that_call_only(m):
             hs, hq = host(s), host(q)
             assert (hs[:M] == 0x7F).all() and not hs[M:].any(), kind
             assert not hq.any(), kind
+            assert m.workspace_timeouts(ws) == i + 1, kind  # one count per abandoned launch
     finally:
         assert m.set_barrier_timeout_us(previous) == 0
     ts, a, q, s = outputs()
@@ -265,6 +267,7 @@ def test_barrier_timeout_gives_nan_for_that_call_only(m):
     assert host(ts)[0] == s_g and host(a)[0] == amax
     assert np.array_equal(host(s), os_), first_mismatch(host(s), os_)
     assert np.array_equal(host(q), oq), first_mismatch(host(q), oq)
+    assert m.workspace_timeouts(ws) == 3  # sticky; a completed launch leaves it
     del keep
 
 

@@ -88,6 +88,35 @@ def test_ring_small_ragged_chunks_and_segments(m):
     assert ok, worst
 
 
+@pytest.mark.parametrize("M,chunk,slots", [(300, 512, 1), (1000, 320, 1), (1000, 320, 2), (129, 64, 3)])
+def test_ring_edge_shapes(m, M, chunk, slots):
+    """One chunk larger than M, chunks that are not a multiple of the GEMM's
+    256-row tile (outputs within tolerance, not bit-equal to the chained path
+    there), chunks of 64 rows; slot bytes checked with one slot per chunk."""
+    dev = device()
+    K, N = 192, 272
+    x = synth.normal_bf16(73, 0, (M, K), 1.0)
+    sh = synth.normal_bf16(73, 1, (2, K), 0.1)
+    sc = synth.normal_bf16(73, 2, (2, K), 0.1)
+    W = synth.normal_bf16(73, 3, (N, K), 0.02)
+    rs = [0, M // 3, M]
+    xd, shd, scd = to_dev_u16(x), to_dev_u16(sh), to_dev_u16(sc)
+    qw, sfw, tw = m.quantize_weight(to_dev_u16(W))
+    seg = oracle.Segments(rs, sh, sc)
+    s_g, oq, osf, _ = _par.modulate_quantize(x, seg, oracle.padded_rows(M))
+    chunks = -(-M // chunk)
+    out_all, ts, _, ring = m.modulate_gemm_ring(xd, rs, shd, scd, qw, sfw, tw, chunk_rows=chunk, slots=chunks)
+    out, _, _, _ = m.modulate_gemm_ring(xd, rs, shd, scd, qw, sfw, tw, chunk_rows=chunk, slots=slots)
+    torch.cuda.synchronize()
+    assert host(ts)[0] == np.float32(s_g)
+    check_slots(ring, chunk, M, K, oq, osf)
+    assert torch.equal(out.view(torch.int16), out_all.view(torch.int16))
+    sw, oqw, osfw, _ = _par.quantize_bf16(W)
+    ref = _par.gemm_rows(oq, osf, s_g, oqw, osfw, sw, np.arange(M))
+    ok, worst = oracle.gemm_tolerance_ok(out_f64(out), ref)
+    assert ok, worst
+
+
 def test_ring_qkv_canonical_19_chunks(m):
     """The QKV projection at M = 37,810 in 2048-row chunks (18 full chunks and
     a last one of 946 rows): each chunk's slot bytes against the oracle's

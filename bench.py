@@ -56,6 +56,10 @@ def parse():
                    help="before timing, copy 1 GiB once (a plain copy kernel of known size, for scaling "
                         "rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     p.add_argument("--summarize-trace", metavar="DIR", help="print the kernel table of a rocprofv3 trace run")
+    p.add_argument("--skip-steps", type=int, default=0,
+                   help="summaries: leave out the first N steps' calls (the run's warm-up steps)")
+    p.add_argument("--bench-json", metavar="FILE",
+                   help="summaries: a bench.py output line from the same node, set beside the profiled times")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarize FETCH_SIZE/WRITE_SIZE runs and write profiles/traffic.json")
     p.add_argument("--summarize-counters", metavar="DIR",
@@ -95,13 +99,13 @@ def traffic_entry(kernel: str, source_hash: str):
 def main():
     args = parse()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace))
+        print(summarize_trace(args.summarize_trace, args.skip_steps, args.bench_json))
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic))
         return
     if args.summarize_mfma:
-        print(summarize_mfma(args.summarize_mfma))
+        print(summarize_mfma(args.summarize_mfma, args.skip_steps))
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
@@ -729,7 +733,12 @@ def _short(name):
     return name.split("(")[0].replace("void ", "")
 
 
-def summarize_trace(d):
+def _bench_line(path):
+    with open(path) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def summarize_trace(d, skip=0, bench_json=None):
     import numpy as np
 
     stats = _csv_rows(d, "kernel_stats.csv")
@@ -745,8 +754,10 @@ def summarize_trace(d):
     per = {p: [] for p in PROJ}
     for p, c in calls:
         per[p].append(sum(c))
+    per = {p: v[skip:] for p, v in per.items()}
     gem = [u for p in PROJ for u in per[p]]
-    out += ["", "GEMM calls (main launch plus, for FC2, the K-split launch and the finalize launch):", "",
+    out += ["", "GEMM calls (main launch plus, for FC2, the K-split launch and the finalize launch)"
+            + (f", the {skip} warm-up steps left out" if skip else "") + ":", "",
             "| GEMM call | M, N, K | calls | mean us | TFLOP/s | % of 2516.6 |", "|---|---|---|---|---|---|"]
     tot_f = tot_us = 0.0
     for p in PROJ:
@@ -761,6 +772,33 @@ def summarize_trace(d):
     if tot_us:
         tf = tot_f / (tot_us * 1e-6) / 1e12
         out.append(f"| all | | {len(gem)} | {tot_us / len(gem):.1f} | {tf:.1f} | {100 * tf / MFMA_F16_PEAK_TFLOPS:.1f} |")
+    # the step's producer launches, in dispatch order: modulation (QKV, FC1) and SwiGLU (FC2)
+    tr = sorted(trace, key=lambda r: int(r["Dispatch_Id"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    mod = [dur(r) for r in tr if "modulate_quantize_kernel<false>" in r["Kernel_Name"]]
+    fill = [dur(r) for r in tr if "silu_lut_fill_kernel" in r["Kernel_Name"]]
+    sw = [dur(r) for r in tr if "swiglu_quantize_kernel" in r["Kernel_Name"]]
+    # the FC2 producer call is the silu table fill and the single launch
+    prod = {"qkv": mod[0::2][skip:], "fc1": mod[1::2][skip:],
+            "fc2": [a + b for a, b in zip(fill, sw)][skip:]}
+    bench = _bench_line(bench_json) if bench_json else None
+    out += ["", "The step's launches, median over the profiled steps" + (f" after the {skip} warm-up steps" if skip
+                                                                        else "")
+            + (", beside the bench line of the same node (HIP events on the launch stream, p50)" if bench else "")
+            + ":", "",
+            "| launch | profiled steps | median us | bench p50 us | profiled / bench |", "|---|---|---|---|---|"]
+    for p in PROJ:
+        for kind, vals in (("quantize", prod[p]), ("gemm", per[p])):
+            if not vals:
+                continue
+            med = float(np.median(vals))
+            b = bench["timing"]["launch_ms_in_step"].get(f"{p}.{kind}", {}).get("p50") if bench else None
+            bcol = f"{b * 1e3:.1f} | {med / (b * 1e3):.4f}" if b else " | "
+            out.append(f"| {p}.{kind} | {len(vals)} | {med:.1f} | {bcol} |")
+    if bench:
+        out += ["", f"Bench line of the same node: {bench['ms_per_step']} ms per step, value {bench['value']} "
+                    f"{bench['unit']}, roofline frac {bench['roofline']['frac']} "
+                    f"(achieved {bench['roofline']['achieved']} of {bench['roofline']['peak']} TFLOP/s)."]
     return "\n".join(out)
 
 
@@ -884,7 +922,7 @@ def summarize_counters(d):
     return "\n".join(out)
 
 
-def summarize_mfma(d):
+def summarize_mfma(d, skip=0):
     """Per GEMM launch: mean engine clock (GRBM_GUI_ACTIVE summed over the 8
     XCDs / duration) and MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES summed over the
     1024 SIMDs / 1024 / active cycles).  A v_mfma_f32_32x32x16_f16 keeps a
@@ -906,6 +944,7 @@ def summarize_mfma(d):
         for key in ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES"):
             tot[key] = sum(x.get(key, 0.0) for x in c)
         per[p].append(tot)
+    per = {p: v[skip:] for p, v in per.items()}
     out = ["| GEMM call | calls | mean us (profiled) | clock GHz | MFMA busy | implied TFLOP/s | measured TFLOP/s |",
            "|---|---|---|---|---|---|---|"]
     for p in PROJ:

@@ -96,6 +96,21 @@ def traffic_entry(kernel: str, source_hash: str):
         return None
 
 
+def producer_counter_bytes(kind: str):
+    """FETCH_SIZE + WRITE_SIZE bytes per launch of the single-launch producer
+    (the rows held on chip are not read twice, so fewer than the algorithmic
+    bytes), if measured on the current producer source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        e = json.load(open(path)).get("producer_single_launch")
+        if not e or e.get("source_hash") != src_hash("producer.hip", "nvfp4_device.h"):
+            return None
+        b = e["per_launch_bytes"].get(kind)
+        return None if b is None else {"fetch": b["fetch"], "write": b["write"], "total": b["fetch"] + b["write"]}
+    except Exception:
+        return None
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -317,6 +332,9 @@ def main():
         "producer": {
             nme: {"ms": round(prod_ms[nme], 4), "launches": {k.split(".")[1]: round(med[k], 4) for k in prod_parts(nme)},
                   "bytes": prod_bytes[nme],
+                  "bytes_definition": "algorithmic: two reads of the input, QDATA and SFA written (padding rows "
+                                      "included); GBps and frac_hbm divide these by the time",
+                  "counter_bytes": producer_counter_bytes("swiglu" if nme == "fc2" else "modulate"),
                   "GBps": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9, 1),
                   "frac_hbm": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             for nme in flops
@@ -879,10 +897,22 @@ def summarize_traffic(fetch_dir, write_dir):
         n = _short(e["name"])
         if (n, e["grid"]) in prod:
             prod[(n, e["grid"])]["write"].append(e["v"] * ws * 1024)
+    prod_entry = {}
     for (n, g), e in prod.items():
         fm = float(np.mean(e["fetch"])) if e["fetch"] else 0.0
         wm = float(np.mean(e["write"])) if e["write"] else 0.0
         out.append(f"| {n.replace('nvfp4::', '')} | grid {g} | {fm / 1e6:.1f} | {wm / 1e6:.1f} | |")
+        # the step's producer launches (256 workgroups of 1024 or 896 threads)
+        if "modulate_quantize_kernel<false>" in n and g == 256 * 1024:
+            prod_entry["modulate"] = {"fetch": int(fm), "write": int(wm)}
+        elif "swiglu_quantize_kernel" in n and g == 256 * 896:
+            prod_entry["swiglu"] = {"fetch": int(fm), "write": int(wm)}
+    if prod_entry:
+        data["producer_single_launch"] = {
+            "source_hash": src_hash("producer.hip", "nvfp4_device.h"), "per_launch_bytes": prod_entry,
+            "note": "FETCH_SIZE / WRITE_SIZE of the step's single-launch producers, scaled like the GEMM's"}
+        with open(path, "w") as fh:
+            json.dump(data, fh, indent=1)
     out.append("")
     out.append(f"profiles/traffic.json: gemm_kernel bytes_per_launch {int(bpl)} (source hash {entry['source_hash']})")
     return "\n".join(out)

@@ -182,7 +182,9 @@ nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, in
  * library's code object, one copy per device (held until the process ends);
  * every shape nvfp4_modulate_quantize accepts fits it.  The call enqueues a
  * small kernel that zeroes those words, then the producer, on `stream`; it
- * calls no allocator.  All calls on one device share the array: calls that
+ * calls no allocator.  Because the words are cleared by a kernel, a call
+ * captured into a graph replays correctly (make one call outside capture
+ * first: it looks up the array's address and the grid size).  All calls on one device share the array: calls that
  * can overlap in time on one device (two streams without ordering between
  * them) race and must not be made.  Same arguments, requirements and errors
  * as nvfp4_modulate_quantize, without the workspace. */

@@ -1,8 +1,10 @@
 """nvfp4_modulate_quantize_noalloc against nvfp4_modulate_quantize: the same
 tensor scale, amax, QDATA and SFA bytes, through the C ABI, on consecutive
 calls (the second on a smaller input, so that words left by the first call in
-the shared scratch would show), and on the two-pass form it falls back to for
-rows wider than 16,384 values."""
+the shared scratch would show), on the two-pass form it falls back to for
+rows wider than 16,384 values, and captured into a graph: every replay, with
+new contents in the same input buffer and eager work and synchronizations
+between the replays, matches the workspace entry point run eagerly."""
 import numpy as np
 import pytest
 import torch
@@ -92,3 +94,53 @@ def test_noalloc_rejects_bad_arguments_before_launch(m):
     with pytest.raises(m.Nvfp4Error):
         m.nvfp4_modulate_quantize_noalloc(x, 64, 48, 48, bad, ts, am, q, s, 64)   # rows do not end at M
     del keep, keep2
+
+
+def test_noalloc_graph_replays_match_eager(m):
+    dev = device()
+    M, D, cut = 12000, 5376, 7000  # about 16 row groups per workgroup: both streamed and held rows
+    M_pad = m.padded_rows(M)
+    sh = to_dev_u16(synth.normal_bf16(91, 1, (2, D), 0.1))
+    sc = to_dev_u16(synth.normal_bf16(91, 2, (2, D), 0.1))
+    seg, keep = m.make_segments([0, cut, M], sh, sc)
+    x = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    q = torch.empty((M_pad, D // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M_pad, D // 16), dtype=torch.uint8, device=dev)
+
+    def fill(seed):
+        x.copy_(to_dev_u16(synth.add_outliers_t3(synth.normal_bf16(seed, 0, (M, D), 1.0), seed, 0.001, 20.0)))
+
+    def eager_reference():
+        rts = torch.empty(1, dtype=torch.float32, device=dev)
+        ram = torch.empty(1, dtype=torch.float32, device=dev)
+        rq = torch.empty((M_pad, D // 2), dtype=torch.uint8, device=dev)
+        rs = torch.empty((M_pad, D // 16), dtype=torch.uint8, device=dev)
+        m.nvfp4_modulate_quantize(x, M, D, D, seg, m.workspace(dev), rts, ram, rq, rs, M_pad)
+        torch.cuda.synchronize()
+        return host(rts), host(ram), host(rq), host(rs)
+
+    fill(100)
+    # an eager call first: the scratch address and the grid size are looked up outside capture
+    m.nvfp4_modulate_quantize_noalloc(x, M, D, D, seg, ts, amax, q, s, M_pad)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):  # captured on the graph's own stream, the current one inside
+        m.nvfp4_modulate_quantize_noalloc(x, M, D, D, seg, ts, amax, q, s, M_pad)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((101, 102, 103, 104)):
+        print(f"replay {rep} with input seed {seed}", flush=True)
+        fill(seed)
+        torch.cuda.synchronize()
+        want = eager_reference()  # eager work between the replays
+        q.fill_(0xA5)
+        s.fill_(0x5A)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (host(ts), host(amax), host(q), host(s))
+        assert got[0].view(np.uint32)[0] == want[0].view(np.uint32)[0], (rep, "tensor scale")
+        assert got[1].view(np.uint32)[0] == want[1].view(np.uint32)[0], (rep, "amax")
+        assert np.array_equal(got[3], want[3]), (rep, "SFA", first_mismatch(got[3], want[3]))
+        assert np.array_equal(got[2], want[2]), (rep, "QDATA", first_mismatch(got[2], want[2]))
+    del g, keep

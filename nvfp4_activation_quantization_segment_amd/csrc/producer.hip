@@ -404,7 +404,10 @@ __global__ __launch_bounds__(1024) void swiglu_absmax_kernel(const uint16_t* __r
 // the working set and the barrier's helper with no spill inside a loop (the
 // modulation keeps column parameters live).
 constexpr int hold_regs(bool plain) { return plain ? 9 : 7; }
-constexpr int kModHoldLdsBytes = 152 * 1024;  // LDS for held groups (modulation)
+// LDS for held groups (modulation): 32 bytes per active thread and group; at
+// D = 5376 (1008 active threads) five groups, with the divisor table and the
+// barrier's words beside them within the 160 KB.
+constexpr int kModHoldLdsBytes = 158 * 1024;
 
 // Column parameters of one 16-column block as bf16 pairs: bf16(scale+1) and
 // shift of columns 2j (low half) and 2j+1 (high half).
@@ -673,14 +676,16 @@ __device__ __forceinline__ HoldSplit hold_split(int64_t groups, int hold_lds, in
     return h;
 }
 
-// LDS slot of held group h for thread idx: [h][half][idx] in 16-byte words.
-__device__ __forceinline__ void hold_put(uint4* hold, int h, const uint32_t y[8]) {
-    hold[(2 * h) * blockDim.x + threadIdx.x] = make_uint4(y[0], y[1], y[2], y[3]);
-    hold[(2 * h + 1) * blockDim.x + threadIdx.x] = make_uint4(y[4], y[5], y[6], y[7]);
+// LDS slot of held group h for thread idx: [h][half][idx] in 16-byte words,
+// `active` (the R x blocks-per-row threads that own a block) slots per half,
+// so that the idle threads of a workgroup take no LDS.
+__device__ __forceinline__ void hold_put(uint4* hold, int active, int h, const uint32_t y[8]) {
+    hold[(2 * h) * active + threadIdx.x] = make_uint4(y[0], y[1], y[2], y[3]);
+    hold[(2 * h + 1) * active + threadIdx.x] = make_uint4(y[4], y[5], y[6], y[7]);
 }
-__device__ __forceinline__ void hold_get(const uint4* hold, int h, uint32_t y[8]) {
-    const uint4 a = hold[(2 * h) * blockDim.x + threadIdx.x];
-    const uint4 c = hold[(2 * h + 1) * blockDim.x + threadIdx.x];
+__device__ __forceinline__ void hold_get(const uint4* hold, int active, int h, uint32_t y[8]) {
+    const uint4 a = hold[(2 * h) * active + threadIdx.x];
+    const uint4 c = hold[(2 * h + 1) * active + threadIdx.x];
     y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
     y[4] = c.x; y[5] = c.y; y[6] = c.z; y[7] = c.w;
 }
@@ -903,7 +908,7 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
         for (int h = hs.nl - 1; h >= 0; --h) {
             const int r = r_first + (hs.ns + h) * gstride;
             uint32_t y[8];
-            hold_get(hold, h, y);
+            hold_get(hold, g.R * (g.C8 >> 1), h, y);
             pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow, b);
         }
     }
@@ -1018,7 +1023,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                 modulate16_pk(v, cp, y);
             }
             max16(m2, y);
-            hold_put(hold, tl - hs.ns, y);
+            hold_put(hold, g.R * C16, tl - hs.ns, y);
         }
     }
     // streamed groups, two per iteration, with binary32 column parameters
@@ -1458,7 +1463,7 @@ hipError_t launch_swiglu_quantize(const uint16_t* gate, const uint16_t* up, cons
 hipError_t launch_modulate_quantize(const uint16_t* x, const RowGeo& g, const SegParams& seg, uint32_t* ws,
                                     float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, bool plain,
                                     const BarrierArgs& ba, hipStream_t s) {
-    const int hold_lds = kModHoldLdsBytes / (32 * g.block);
+    const int hold_lds = kModHoldLdsBytes / (32 * g.R * (g.C8 >> 1));
     if (plain)
         hipLaunchKernelGGL(modulate_quantize_kernel<true>, dim3(g.grid), dim3(g.block), 0, s, x, g, seg, ws,
                            tensor_scale, amax_out, qdata, sfa, hold_lds, ba);

@@ -37,6 +37,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// Raises the workgroup's shared threshold word (float bits; the values are
+// non-negative or NaN, which order as their bit patterns) with this wave's
+// largest mf and returns the new value, the same in every lane.
+__device__ __forceinline__ float raise_threshold(uint32_t* word, float mf) {
+    const uint32_t w = wave_max_u32(__float_as_uint(mf));
+    uint32_t v = 0;
+    if ((threadIdx.x & 63) == 0) v = atomicMax(word, w);
+    v = (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+    return __uint_as_float(v > w ? v : w);
+}
+
 // Workgroup maximum of a 16-bit magnitude, then the grid-level finish: one
 // atomic max per workgroup; the last workgroup to take a ticket turns the
 // maximum into the tensor scale and returns the workspace to zero.
@@ -743,6 +754,41 @@ __device__ __forceinline__ float mod16_max(const uint4& a, const uint4& c, const
     return m;
 }
 
+// Largest |bf16(scale+1)| and largest |shift| over a block's 16 columns (NaN if
+// any is NaN).
+struct ColBound {
+    float S, H;
+};
+__device__ __forceinline__ ColBound col_bound(const ColParams& p0, const ColParams& p1) {
+    ColBound cb = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        cb.S = __builtin_elementwise_maximum(
+            cb.S, __builtin_elementwise_maximum(__builtin_fabsf(p0.s1[k]), __builtin_fabsf(p1.s1[k])));
+        cb.H = __builtin_elementwise_maximum(
+            cb.H, __builtin_elementwise_maximum(__builtin_fabsf(p0.sh[k]), __builtin_fabsf(p1.sh[k])));
+    }
+    return cb;
+}
+
+// Upper bound on the unrounded modulation sums z = RN32(bf16(x*s1) + sh) of one
+// block's 16 columns in two rows of the same segment: with X the largest |x|
+// (both rows), |z| <= RN32(bf16(X*S) + H), because |x*s1| <= X*S, bf16 and
+// binary32 rounding are monotone and odd, and |p + sh| <= |p| + |sh|.  NaN when
+// an x is NaN (its magnitude bits exceed every finite and infinite one).  A
+// non-finite bound bounds nothing (x = Inf times s1 = 0 is NaN) and is never
+// compared as a bound.
+__device__ __forceinline__ float mod_bound2(const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1,
+                                            const ColBound& cb) {
+    const uint32_t w[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                            b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    uint32_t m2 = mag2(w[0]);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) m2 = pk_max_u16(m2, mag2(w[k]));
+    const float X = __uint_as_float(fold_max(m2) << 16);
+    return round_bf16(X * cb.S) + cb.H;
+}
+
 // y of 16 columns as binary32 values (each exactly a bf16) and the largest
 // magnitude of the unrounded sums (NaN if any sum is NaN).  Rounding to bf16
 // is monotone and odd, so the bf16 rounding of that maximum is the block's
@@ -985,6 +1031,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                                                                  BarrierArgs ba) {
     __shared__ uint4 hold[kModHoldLdsBytes / 16];
     __shared__ float2 dr[128];
+    __shared__ uint32_t thr_word;  // pass 1: a maximum counted by a thread of the workgroup
     const char* xb = reinterpret_cast<const char*>(x);
     const int C16 = g.C8 >> 1;
     const int rho = threadIdx.x / C16, b = threadIdx.x - rho * C16;
@@ -997,6 +1044,8 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     const uint32_t xrow = 2u * (uint32_t)g.ldx, xcol = 32u * (uint32_t)b;
 
     // ---- pass 1 (every thread runs the loops; `on` guards memory accesses) ----
+    if (threadIdx.x == 0) thr_word = 0;
+    __syncthreads();
     uint32_t m2 = 0;
     uint32_t hy[HR][8];
     int s = 0, seg_hi = 0;
@@ -1030,16 +1079,26 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
     // (short of VALU here, not of registers: the held groups come later).
     // EXACT: the maximum of the rounded y's bit patterns (the plain quantizer,
     // and the rare rerun after a NaN); otherwise the maximum of the unrounded
-    // sums (mod16_max), whose bf16 rounding is the same value.
+    // sums (mod16_max), whose bf16 rounding is the same value.  Without EXACT a
+    // wave skips the modulation of a pair of rows when every thread's bound
+    // (mod_bound2) is finite and at most a maximum that a thread of the
+    // workgroup has already counted: those sums cannot raise the maximum.
     auto streamed = [&](auto exact) {
         constexpr bool EXACT = decltype(exact)::value;
+        constexpr bool BOUND = !PLAIN && !EXACT;
         ColParams c0, c1;
+        ColBound cb = {0.0f, 0.0f};
         int hi = 0, sc = 0;
         float mf = 0.0f;
+        float thr = 0.0f;  // wave-uniform
+        auto cols = [&](int s_) {
+            load_cols(seg, s_, 2 * b, c0);
+            load_cols(seg, s_, 2 * b + 1, c1);
+            if constexpr (BOUND) cb = col_bound(c0, c1);
+        };
         if (!PLAIN && on) {
             sc = seg_find(seg, r_first < g.M ? r_first : 0, 0);
-            load_cols(seg, sc, 2 * b, c0);
-            load_cols(seg, sc, 2 * b + 1, c1);
+            cols(sc);
             hi = (int)seg.row_start[sc + 1];
         }
         auto absmax = [&](const uint4& v0, const uint4& v1, int r) {
@@ -1050,8 +1109,7 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
                 if (r >= hi) {
                     sc = seg_find(seg, r, sc);
                     hi = (int)seg.row_start[sc + 1];
-                    load_cols(seg, sc, 2 * b, c0);
-                    load_cols(seg, sc, 2 * b + 1, c1);
+                    cols(sc);
                 }
                 if constexpr (EXACT) {
                     uint32_t y[8];
@@ -1064,11 +1122,27 @@ __global__ __launch_bounds__(1024) void modulate_quantize_kernel(const uint16_t*
         };
         int t = 0;
         for (; t + 1 < hs.ns; t += 2) {
+            const int r0 = r_first + t * gstride, r1 = r0 + gstride;
+            uint4 a0, a1, b0, b1;
+            bool bounded = true;
             if (on) {
-                const int r0 = r_first + t * gstride, r1 = r0 + gstride;
                 const uint32_t o0 = (uint32_t)r0 * xrow + xcol, o1 = (uint32_t)r1 * xrow + xcol;
-                const uint4 a0 = ld16o(xb, o0), a1 = ld16o(xb, o0 + 16), b0 = ld16o(xb, o1),
-                            b1 = ld16o(xb, o1 + 16);
+                a0 = ld16o(xb, o0);
+                a1 = ld16o(xb, o0 + 16);
+                b0 = ld16o(xb, o1);
+                b1 = ld16o(xb, o1 + 16);
+                if constexpr (BOUND) {
+                    const float B = mod_bound2(a0, a1, b0, b1, cb);
+                    bounded = r1 < hi && B <= thr && B <= 0x1.fffffep127f;
+                }
+            }
+            if constexpr (BOUND) {
+                if (!__all(bounded) && on) {
+                    absmax(a0, a1, r0);
+                    absmax(b0, b1, r1);
+                }
+                if (((t >> 1) & 3) == 0) thr = raise_threshold(&thr_word, mf);
+            } else if (on) {
                 absmax(a0, a1, r0);
                 absmax(b0, b1, r1);
             }

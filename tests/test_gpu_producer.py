@@ -429,6 +429,53 @@ def test_single_launch_streams_and_holds_rows(m):
     check_modulate(m, x, segs, sh, sc)
 
 
+@pytest.mark.parametrize("kind", ["shift", "scale", "segment", "late", "inf_times_zero"])
+def test_pass1_maximum_from_any_column_segment_or_row(m, kind):
+    """Tensor maxima that a bound on |y| from |x| alone would miss, in rows the
+    single launch streams in pass 1 ([126976, 1024]: 31 row groups of 16 rows
+    per workgroup, the first 20 streamed, two per iteration): a maximum made by
+    one column's shift, by one column's scale, by a row of the second segment
+    whose pass-1 partner row is in the first, by an outlier in a workgroup's
+    last streamed pair, and a NaN from x = Inf times bf16(scale+1) = 0.  Amax
+    bits and tensor scale against the oracle in both launch forms; all bytes
+    for the segment case."""
+    M, D, B0 = 126976, 1024, 41080
+    x = synth.normal_bf16(91, 0, (M, D), 1.0)
+    sh = synth.normal_bf16(91, 1, (2, D), 0.1)
+    sc = synth.normal_bf16(91, 2, (2, D), 0.1)
+    rs = [0, B0, M]
+    if kind == "shift":
+        sh[1, 700] = bf16_np(1000.0)
+    elif kind == "scale":
+        sc[0, 33] = bf16_np(300.0)
+    elif kind == "segment":
+        # row 45091 = group 11 of workgroup 2 (row 3 of 16); its pair row in
+        # group 10, 40995, lies before the segment boundary
+        sc[1, 517] = bf16_np(20.0)
+        x[B0:, 517] = bf16_np(0.01)
+        x[45091, 517] = bf16_np(4.0)
+    elif kind == "late":
+        x[77829, 100] = bf16_np(250.0)   # group 19 of workgroup 0
+    else:
+        sc[0, 900] = bf16_np(-1.0)
+        x[41015, 900] = 0x7F80           # group 10 of workgroup 3
+    print(f"pass-1 maximum case {kind}", flush=True)
+    if kind == "segment":
+        check_modulate(m, x, np.array(rs, np.int64), sh, sc)
+        return
+    seg = oracle.Segments(rs, sh, sc)
+    amax = np.float32(_par.amax_merge(_par._map(lambda r: oracle.modulate_amax_rows(x, seg, *r),
+                                                 _par._ranges(M, 4 * _par.WORKERS))))
+    s_g = np.float32(oracle.tensor_scale(float(amax)))
+    if kind == "inf_times_zero":
+        assert (amax.view(np.uint32) >> 16) > 0x7F80
+    for single in (False, True):
+        gs, _, _, gamax = gpu_modulate(m, x, rs, sh, sc, single_pass=single)
+        path = "single launch" if single else "two passes"
+        assert np.float32(gamax).view(np.uint32) == amax.view(np.uint32), (path, gamax, amax)
+        assert np.float32(gs).view(np.uint32) == s_g.view(np.uint32) or (np.isnan(gs) and np.isnan(s_g)), path
+
+
 def test_weight_prepack_matches_oracle_quantizer(m):
     w = synth.workload("tiny").weight()
     sw, qw, sfw, _ = _par.quantize_bf16(w)

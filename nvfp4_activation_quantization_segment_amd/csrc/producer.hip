@@ -735,6 +735,20 @@ __device__ __forceinline__ float max_abs2(float m, float a, float b) {
     return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b)));
 }
 
+// Largest |s[k]| of 16 values (NaN if any is NaN) as a tree of three-input
+// maxima: 8 v_maximum3_f32 (a running maximum pairs values into 12).
+__device__ __forceinline__ float absmax16(const float s[16]) {
+    auto mx3 = [](float a, float b, float c) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+    };
+    float m[6];
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+        m[i] = mx3(__builtin_fabsf(s[3 * i]), __builtin_fabsf(s[3 * i + 1]), __builtin_fabsf(s[3 * i + 2]));
+    m[5] = __builtin_fabsf(s[15]);
+    return __builtin_elementwise_maximum(mx3(m[0], m[1], m[2]), mx3(m[3], m[4], m[5]));
+}
+
 // Running maximum of the magnitudes of the unrounded modulation sums of 16
 // columns (NaN once any sum is NaN).  bf16 rounding is monotone and odd, so
 // the bf16 rounding of this maximum is the largest |y| of those columns: pass
@@ -796,18 +810,17 @@ __device__ __forceinline__ float mod_bound2(const uint4& a0, const uint4& a1, co
 __device__ __forceinline__ float mod16_f32(const uint4& a, const uint4& c, const ColParams& p0,
                                            const ColParams& p1, float y[16]) {
     const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    float m = 0.0f;
+    float z[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const ColParams& p = j < 4 ? p0 : p1;
         const int k = 2 * (j & 3);
-        const float sa = round_bf16(bf16_lo(xw[j]) * p.s1[k]) + p.sh[k];
-        const float sb = round_bf16(bf16_hi(xw[j]) * p.s1[k + 1]) + p.sh[k + 1];
-        m = max_abs2(m, sa, sb);
-        y[2 * j] = round_bf16(sa);
-        y[2 * j + 1] = round_bf16(sb);
+        z[2 * j] = round_bf16(bf16_lo(xw[j]) * p.s1[k]) + p.sh[k];
+        z[2 * j + 1] = round_bf16(bf16_hi(xw[j]) * p.s1[k + 1]) + p.sh[k + 1];
+        y[2 * j] = round_bf16(z[2 * j]);
+        y[2 * j + 1] = round_bf16(z[2 * j + 1]);
     }
-    return m;
+    return absmax16(z);
 }
 
 // bf16 magnitude bits of a block's maximum from the maximum m of its
@@ -829,14 +842,12 @@ __device__ __forceinline__ uint32_t block_amax_bits(float m, const float y[16]) 
 // and their largest magnitude (NaN if any value is NaN).
 __device__ __forceinline__ float plain16_f32(const uint4& a, const uint4& c, float y[16]) {
     const uint32_t xw[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         y[2 * j] = bf16_lo(xw[j]);
         y[2 * j + 1] = bf16_hi(xw[j]);
-        m = max_abs2(m, y[2 * j], y[2 * j + 1]);
     }
-    return m;
+    return absmax16(y);
 }
 
 // Scale and codes of one block given as binary32 values and the maximum from
@@ -858,16 +869,15 @@ __device__ __forceinline__ float swiglu16_f32(const uint16_t* lut, const uint4& 
                                               const uint4& u0, const uint4& u1, float h[16]) {
     const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    float m = 0.0f;
+    float z[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float sa = __uint_as_float((uint32_t)lut[gw[j] & 0xFFFFu] << 16) * bf16_lo(uw[j]);
-        const float sb = __uint_as_float((uint32_t)lut[gw[j] >> 16] << 16) * bf16_hi(uw[j]);
-        m = max_abs2(m, sa, sb);
-        h[2 * j] = round_bf16(sa);
-        h[2 * j + 1] = round_bf16(sb);
+        z[2 * j] = __uint_as_float((uint32_t)lut[gw[j] & 0xFFFFu] << 16) * bf16_lo(uw[j]);
+        z[2 * j + 1] = __uint_as_float((uint32_t)lut[gw[j] >> 16] << 16) * bf16_hi(uw[j]);
+        h[2 * j] = round_bf16(z[2 * j]);
+        h[2 * j + 1] = round_bf16(z[2 * j + 1]);
     }
-    return m;
+    return absmax16(z);
 }
 
 // Pass 2 of the SwiGLU producer.  OFF is the offset type: uint32_t when every

@@ -165,6 +165,16 @@ __device__ __forceinline__ uint32_t block_scale_fast(float a16, float s_g, float
     return e4m3_encode(t);
 }
 
+// The same inside a launch that took s_g from the maximum of the very values
+// whose blocks it scales (a16 <= amax, s_g = RN(amax/2688) in the fast range):
+// RN(a16/6) <= RN(amax/6), and its quotient by s_g is at most 448 (1 + 2^-22),
+// so t < 464 always, the first product cannot overflow, and the clamp and
+// NaN test of e4m3_encode never change the code.
+__device__ __forceinline__ uint32_t block_scale_bounded(float a16, float s_g, float rg) {
+    const float t = div_markstein(div_markstein(a16, 6.0f, kRcp6), s_g, rg);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xFFu;
+}
+
 // Reference-form block scale with two correctly rounded divisions (any input).
 __device__ __forceinline__ uint32_t block_scale_slow(float a16, float s_g) {
     float u = a16 / 6.0f;
@@ -255,13 +265,22 @@ __device__ __forceinline__ void build_dr_table(float2* dr, float s_g) {
     __syncthreads();
 }
 
+// BOUNDED: the block maximum is at most the maximum s_g was taken from
+// (block_scale_bounded).  A tensor scale in the fast range then also means
+// that maximum, and so every block, is finite: the choice of path is the same
+// for every block of the launch.
+template <bool BOUNDED = false>
 __device__ __forceinline__ BlockQ block_setup_tab(uint32_t amax_bits16, float s_g, float rg, bool sg_fast,
                                                   const float2* dr) {
     BlockQ b;
     float a16 = __uint_as_float(amax_bits16 << 16);
-    bool finite = amax_bits16 < 0x7F80u;
-    b.fast = sg_fast && finite;
-    b.sf = b.fast ? block_scale_fast(a16, s_g, rg) : block_scale_slow(a16, s_g);
+    b.fast = BOUNDED ? sg_fast : sg_fast && amax_bits16 < 0x7F80u;
+    if (!b.fast)
+        b.sf = block_scale_slow(a16, s_g);
+    else if constexpr (BOUNDED)
+        b.sf = block_scale_bounded(a16, s_g, rg);
+    else
+        b.sf = block_scale_fast(a16, s_g, rg);
     const float2 t = dr[b.sf];
     b.d = t.x;
     b.r = t.y;

@@ -107,12 +107,13 @@ __device__ __forceinline__ void store_block(const PackedBlock& pb, uint8_t* __re
     *sf = (uint8_t)pb.sf;
 }
 
+template <bool BOUNDED = false>
 __device__ __forceinline__ PackedBlock pack_block16(const uint32_t y[8], float s_g, float rg, bool sg_fast,
                                                     const float2* dr) {
     uint32_t m2 = mag2(y[0]);
 #pragma unroll
     for (int k = 1; k < 8; ++k) m2 = pk_max_u16(m2, mag2(y[k]));
-    const BlockQ bq = block_setup_tab(fold_max(m2), s_g, rg, sg_fast, dr);
+    const BlockQ bq = block_setup_tab<BOUNDED>(fold_max(m2), s_g, rg, sg_fast, dr);
     PackedBlock pb;
     pb.w.x = quantize8(y, bq.d, bq.r, bq.fast) & bq.keep;
     pb.w.y = quantize8(y + 4, bq.d, bq.r, bq.fast) & bq.keep;
@@ -120,10 +121,11 @@ __device__ __forceinline__ PackedBlock pack_block16(const uint32_t y[8], float s
     return pb;
 }
 
+template <bool BOUNDED = false>
 __device__ __forceinline__ void pack_block16_store(const uint32_t y[8], float s_g, float rg, bool sg_fast,
                                                    const float2* dr, uint8_t* __restrict__ qrow,
                                                    uint8_t* __restrict__ srow, int b) {
-    store_block(pack_block16(y, s_g, rg, sg_fast, dr), qrow + 8 * b, srow + b);
+    store_block(pack_block16<BOUNDED>(y, s_g, rg, sg_fast, dr), qrow + 8 * b, srow + b);
 }
 
 // ---------------------------------------------------------------------------
@@ -852,9 +854,10 @@ __device__ __forceinline__ float plain16_f32(const uint4& a, const uint4& c, flo
 
 // Scale and codes of one block given as binary32 values and the maximum from
 // mod16_f32.
+template <bool BOUNDED = false>
 __device__ __forceinline__ PackedBlock pack16f(const float y[16], float m, float s_g, float rg, bool sg_fast,
                                                const float2* dr) {
-    const BlockQ bq = block_setup_tab(block_amax_bits(m, y), s_g, rg, sg_fast, dr);
+    const BlockQ bq = block_setup_tab<BOUNDED>(block_amax_bits(m, y), s_g, rg, sg_fast, dr);
     PackedBlock pb;
     pb.w.x = quantize8f(y, bq.d, bq.r, bq.fast) & bq.keep;
     pb.w.y = quantize8f(y + 8, bq.d, bq.r, bq.fast) & bq.keep;
@@ -958,14 +961,14 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
         for (int h = 0; h < HR; ++h) {
             const int r = r_first + (t0 + h) * gstride;
             if (h < hs.nr && r < g.M)
-                pack_block16_store(hy[h], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
+                pack_block16_store<true>(hy[h], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
                                    b);
         }
         for (int h = hs.nl - 1; h >= 0; --h) {
             const int r = r_first + (hs.ns + h) * gstride;
             uint32_t y[8];
             hold_get(hold, g.R * (g.C8 >> 1), h, y);
-            pack_block16_store(y, s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow, b);
+            pack_block16_store<true>(y, s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow, b);
         }
     }
     int t = hs.ns - 1;
@@ -993,7 +996,7 @@ __device__ __forceinline__ void pass2_mod(const char* __restrict__ xb, const Row
             }
             m = mod16_f32(v0, v1, c0, c1, y);
         }
-        return pack16f(y, m, s_g, rg, sg_fast, dr);
+        return pack16f<true>(y, m, s_g, rg, sg_fast, dr);
     };
     auto put = [&](const PackedBlock& pb, int r) {
         store_block(pb, qdata + ((uint32_t)r * qrow + qcol), sfa + ((uint32_t)r * srow + b));
@@ -1352,7 +1355,7 @@ __global__ __launch_bounds__(1024) void swiglu_quantize_kernel(const uint16_t* _
         for (int k = 0; k < HR; ++k) {
             const int r = r_first + (hs.ns + k) * gstride;
             if (k < hs.nr && r < g.M)
-                pack_block16_store(hy[k], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
+                pack_block16_store<true>(hy[k], s_g, rg, sg_fast, dr, qdata + (uint32_t)r * qrow, sfa + (uint32_t)r * srow,
                                    b);
         }
     }
@@ -1362,7 +1365,7 @@ __global__ __launch_bounds__(1024) void swiglu_quantize_kernel(const uint16_t* _
     auto pack = [&](const uint4& g0, const uint4& g1, const uint4& u0, const uint4& u1) {
         float h[16];
         const float m = swiglu16_f32(slut, g0, g1, u0, u1, h);
-        return pack16f(h, m, s_g, rg, sg_fast, dr);
+        return pack16f<true>(h, m, s_g, rg, sg_fast, dr);
     };
     // Streamed groups last to first, two per iteration, as in the modulation
     // single launch: the next pair's loads ahead of this pair's stores, and a

@@ -476,6 +476,24 @@ def test_pass1_maximum_from_any_column_segment_or_row(m, kind):
         assert np.float32(gs).view(np.uint32) == s_g.view(np.uint32) or (np.isnan(gs) and np.isnan(s_g)), path
 
 
+@pytest.mark.parametrize("M", [12001, 769])
+@pytest.mark.parametrize("amax", [2688.0, 13.125])
+def test_tensor_scales_with_short_binary_expansions(m, amax, M):
+    """Tensor maxima that make s_g a power of two (2688: s_g = 1, so every
+    divisor is an E4M3 value and many quotients fall exactly on E2M1
+    midpoints) or a short binary fraction (13.125 = 210/16: s_g = 2^-8 * 5/4),
+    with ragged row counts that leave rows past M in the last row group.  Bytes
+    against the oracle for the modulation producer (both launch forms) and the
+    plain quantizer."""
+    D = 5376
+    x = synth.normal_bf16(97, 0, (M, D), 1.0)
+    x[M // 2, 1234] = bf16_np(amax)
+    print(f"short-expansion scales: amax {amax} M {M}", flush=True)
+    s_g = check_values(m, x)
+    assert s_g in (np.float32(1.0), np.float32(2.0 ** -8 * 1.25))
+    check_plain(m, x)
+
+
 def test_weight_prepack_matches_oracle_quantizer(m):
     w = synth.workload("tiny").weight()
     sw, qw, sfw, _ = _par.quantize_bf16(w)

@@ -108,7 +108,10 @@ def test_step_block_scale_all_maxima(m):
 
 def test_step_element_code_all_values(m):
     """Every bf16 y against every E4M3 block scale (0, all finite codes and the
-    NaN code) for tensor scales across the range."""
+    NaN code) for tensor scales across the range, and for maxima whose 8-bit
+    mantissa shares a factor 3 or 7 with 2688 = 2^7 * 3 * 7 (168, 210, 252,
+    140; s_g = 1 at 2688), where s_g is a short or short-period binary
+    fraction and quotients fall exactly on or next to E2M1 midpoints."""
     y = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     y = y[(y & 0x7FFF) <= 0x7F80]  # finite values and +-inf
     sfs = np.arange(0, 0x80, dtype=np.uint8)
@@ -117,7 +120,8 @@ def test_step_element_code_all_values(m):
     y_dev, s_dev = to_dev_u16(Y), to_dev(S)
     code = torch.empty(Y.size, dtype=torch.uint8, device=device())
     sg_dev = torch.empty(1, dtype=torch.float32, device=device())
-    for s_g in _scales()[::3]:
+    structured = [0x4528, 0x3FD2, 0x27D2, 0x4128, 0x31FC, 0x2E8C]
+    for s_g in _scales() + [oracle.tensor_scale(float(bf16_values(b))) for b in structured]:
         sg_dev.fill_(s_g)
         m.nvfp4_step_element_code(y_dev, s_dev, sg_dev, code, Y.size)
         _sync()

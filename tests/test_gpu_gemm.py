@@ -201,6 +201,62 @@ def test_canonical_projection_sampled_rows(m, name):
     print(f"{name}: worst err/bound {worst:.3g}", flush=True)
 
 
+def _decoded(q, sf, rows, K, e2m1):
+    """Exact binary32 values of packed rows: E2M1 codes (low nibble first)
+    through the published value set, times the E4M3 scale of each 16."""
+    codes = torch.stack([(q[:rows] & 0xF).long(), (q[:rows] >> 4).long()], dim=-1).reshape(rows, K)
+    scale = sf[:rows].view(torch.float8_e4m3fn).to(torch.float32).repeat_interleave(16, dim=1)
+    return e2m1[codes] * scale
+
+
+@pytest.mark.parametrize("name", ["qkv", "fc1", "fc2"])
+def test_canonical_projection_every_output_against_fp32_product(m, name):
+    """Every output of the projection at M = 37,810 (the launches bench.py
+    times: main, K-split tail and finalize) against a binary32 product of the
+    exactly decoded operands, under the same tolerance with the rms taken over
+    all outputs.  The product is torch's fp32 matmul on the GPU (TF32 off); the
+    decode uses the published E2M1 values and torch's float8 decode, and each
+    decoded value is exact in binary32.  The oracle comparison samples rows;
+    this reaches every tile, the ragged last row tile and the split tail tiles
+    included.  The packed operands are the producer's and the weight
+    quantizer's, whose bytes the producer tests compare with the oracle."""
+    import json
+    import os
+
+    w = synth.workload(name)
+    dev = device()
+    print(f"{name}: every output, M={w.M} K={w.K} N={w.N}", flush=True)
+    if w.kind == "modulate":
+        rs, sh, sc = w.segments()
+        q, s, ts, _ = m.modulate_quantize(to_dev_u16(w.x()), rs, to_dev_u16(sh), to_dev_u16(sc))
+    else:
+        q, s, ts, _ = m.swiglu_quantize(to_dev_u16(w.gate_up()))
+    qw, sfw, tw = m.quantize_weight(to_dev_u16(w.weight()))
+    out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    m.gemm(q, s, ts, w.M, qw, sfw, tw, out=out)
+    torch.cuda.synchronize()
+    with open(os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.json")) as f:
+        mags = json.load(f)["values"]
+    e2m1 = torch.tensor(mags + [-v for v in mags], dtype=torch.float32, device=dev)
+    alpha = torch.tensor(np.float32(host(ts)[0]) * np.float32(host(tw)[0]), dtype=torch.float32, device=dev)
+    wdec = _decoded(qw, sfw, w.N, w.K, e2m1)
+    tf32 = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    try:
+        excess, sumsq = -np.inf, 0.0
+        for r0 in range(0, w.M, 4096):
+            r1 = min(w.M, r0 + 4096)
+            ref = (_decoded(q[r0:], s[r0:], r1 - r0, w.K, e2m1) @ wdec.t()) * alpha
+            got = out[r0:r1].float()
+            excess = max(excess, float(((got - ref).abs() - 2.0 ** -7 * ref.abs()).max()))
+            sumsq += float((ref.double() ** 2).sum())
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = tf32
+    rms = (sumsq / (w.M * w.N)) ** 0.5
+    print(f"{name}: worst excess over 2^-7|ref| {excess:.3g}, 1e-3 rms {1e-3 * rms:.3g}", flush=True)
+    assert excess <= 1e-3 * rms, (excess, rms)
+
+
 def test_scale_rows_misaligned_take_the_word_path(m):
     """K % 256 == 0 lets the kernel fetch scales 16 bytes per row per 4 K
     steps, but only when both scale arrays are 16-byte aligned; scale arrays

@@ -148,21 +148,32 @@ def main():
     wq, wf1, wf2 = synth.workload("qkv"), synth.workload("fc1"), synth.workload("fc2")
     M = wq.M
     M_pad = wq.m_pad
+    # SHA-256 of every generated input (the same as tests/golden/synth_sha256.json)
+    input_sha = {}
+
+    def sha(a):
+        return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
     x_h = wq.x()
+    input_sha["x (qkv, fc1)"] = sha(x_h)
     x = up(x_h)
     segs = {}
     for w in (wq, wf1):
         rs, sh, sc = w.segments()
+        input_sha[f"{w.name} shift"], input_sha[f"{w.name} scale"] = sha(sh), sha(sc)
         segs[w.name] = (rs, up(sh), up(sc))
     gu_h = wf2.gate_up()
+    input_sha["fc2 gate_up"] = sha(gu_h)
     gu = up(gu_h)
     weights = {}
     for w in (wq, wf1, wf2):
-        wt = up(w.weight())
+        wt_h = w.weight()
+        input_sha[f"{w.name} weight"] = sha(wt_h)
+        wt = up(wt_h)
         with torch.cuda.stream(stream):
             weights[w.name] = nv.quantize_weight(wt, stream=stream)
         stream.synchronize()
-        del wt
+        del wt, wt_h
     # outputs and per-projection scratch, allocated once
     bufs = {}
     for w in (wq, wf1, wf2):
@@ -348,6 +359,7 @@ def main():
         "timing": {"wall_ms_timed_region": round(wall_ms, 2), "event_ms_timed_region": round(total_ms, 2),
                    "setup_s": round(setup_s, 1), "kernel_source_hash": gemm_hash,
                    "launch_ms_in_step": launch_pct},
+        "input_sha256": input_sha,
         "output_sha256": hashes,
         "producer_standalone": {
             nme: dict(v, bytes=prod_bytes[nme],

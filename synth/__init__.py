@@ -69,7 +69,19 @@ def _L():
     return _lib
 
 
+_THREADS: int | None = None
+
+
+def set_threads(n: int | None) -> None:
+    """Generate with n threads (None: the default).  The values do not depend
+    on it: every element is a function of its index alone."""
+    global _THREADS
+    _THREADS = n
+
+
 def _threads() -> int:
+    if _THREADS is not None:
+        return max(1, min(64, _THREADS))
     # The GPU host gives one GPU's share of its cores (16); never more.
     try:
         n = len(os.sched_getaffinity(0))
@@ -193,6 +205,23 @@ class Workload:
     def residual(self) -> np.ndarray:
         """Residual stream [M, N] bf16 bits, N(0, 1)."""
         return normal_bf16(self.c_seg, T_RESIDUAL, (self.M, self.N), 1.0)
+
+    def inputs(self) -> dict:
+        """Every generated input of the workload, by name (bf16 bits, except
+        the int64 segment bounds)."""
+        out = {}
+        if self.kind == "swiglu":
+            out["gate_up"] = self.gate_up()
+        else:
+            out["x"] = self.x()
+        if self.kind == "modulate":
+            out["row_start"], out["shift"], out["scale"] = self.segments()
+        if self.N is not None:
+            out["weight"] = self.weight()
+        if self.kind == "plain" and self.N is not None:
+            out["row_start"], out["gate"] = self.gates()
+            out["residual"] = self.residual()
+        return out
 
     def check_rows(self, k: int = 64) -> np.ndarray:
         """GEMM rows checked at full size: boundary rows plus seeded rows."""

@@ -92,8 +92,6 @@ __device__ void reduce_and_finish(uint32_t m16, uint32_t* ws, float* tensor_scal
     }
 }
 
-// One thread, one whole 16-value block: maximum, scale, codes, and the 8
-// QDATA bytes plus the scale byte stored for block b of a row.
 // One block's output: its 8 QDATA bytes and its scale byte.
 struct PackedBlock {
     uint2 w;
@@ -107,6 +105,8 @@ __device__ __forceinline__ void store_block(const PackedBlock& pb, uint8_t* __re
     *sf = (uint8_t)pb.sf;
 }
 
+// One thread, one whole 16-value block given as 8 packed bf16 pairs: maximum,
+// scale and codes (pack_block16_store also stores them for block b of a row).
 template <bool BOUNDED = false>
 __device__ __forceinline__ PackedBlock pack_block16(const uint32_t y[8], float s_g, float rg, bool sg_fast,
                                                     const float2* dr) {
@@ -164,10 +164,6 @@ __device__ __forceinline__ int seg_advance(const SegParams& seg, int64_t r, int 
     return s;
 }
 
-// Rows are assigned grid-stride (workgroup b takes rows b, b+G, b+2G, ...), so
-// the workgroups resident at any moment read one compact window of the tensor
-// that sweeps through it, which is what the memory system streams best.
-// PLAIN: y = x (the plain quantizer; seg is not read).
 // Running maximum of the magnitudes of the unrounded modulation sums of 8
 // columns (NaN once any is NaN); see mod16_max.
 __device__ __forceinline__ float mod8_max(const uint4& xv, const ColParams& cp, float m) {
@@ -182,7 +178,11 @@ __device__ __forceinline__ float mod8_max(const uint4& xv, const ColParams& cp, 
     return m;
 }
 
-// Pass 1 of the modulation producer (and of the plain quantizer).  EXACT: the
+// Pass 1 of the modulation producer (and of the plain quantizer).  Rows are
+// assigned grid-stride (workgroup b takes rows b, b+G, b+2G, ...), so the
+// workgroups resident at any moment read one compact window of the tensor
+// that sweeps through it, which is what the memory system streams best.
+// PLAIN: y = x (seg is not read).  EXACT: the
 // maximum of the rounded y's bf16 magnitude bits; otherwise the maximum of the
 // unrounded sums, whose bf16 rounding is the same value (the kernel reruns the
 // exact form for a thread that met a NaN, so that the largest NaN bit pattern

@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -71,11 +72,24 @@ def parse():
     return p.parse_args()
 
 
+_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_only(text: str) -> str:
+    """C/C++ source without its comments and with every run of whitespace
+    made one space: a comment edit leaves the code, and so this text, as it
+    was (string and character literals are kept as written)."""
+    text = _TOKEN.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return " ".join(text.split())
+
+
 def src_hash(*names):
+    """Hash of the code (comments and layout aside) of the named sources,
+    which identifies the kernels that counter readings were taken on."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "nvfp4_activation_quantization_segment_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "nvfp4_activation_quantization_segment_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -103,7 +117,7 @@ def producer_counter_bytes(kind: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         e = json.load(open(path)).get("producer_single_launch")
-        if not e or e.get("source_hash") != src_hash("producer.hip", "nvfp4_device.h"):
+        if not e or e.get("source_hash") != src_hash("producer.hip", "nvfp4_device.h", "internal.h"):
             return None
         b = e["per_launch_bytes"].get(kind)
         return None if b is None else {"fetch": b["fetch"], "write": b["write"], "total": b["fetch"] + b["write"]}
@@ -304,7 +318,7 @@ def main():
     gemm_achieved = (total_flops / 3) / (gemm_avg_ms * 1e-3) / 1e12
 
     value = total_flops / (ms_per_step * 1e-3) / 1e12
-    gemm_hash = src_hash("gemm.hip", "nvfp4_device.h")
+    gemm_hash = src_hash("gemm.hip", "nvfp4_device.h", "internal.h")
     traffic = traffic_entry("gemm_kernel", gemm_hash)
 
     result = {
@@ -879,7 +893,7 @@ def summarize_traffic(fetch_dir, write_dir):
     bpl = float(np.mean([shapes[p]["fetch"] + shapes[p]["write"] for p in PROJ]))
     entry = {
         "bytes_per_launch": int(bpl),
-        "source_hash": src_hash("gemm.hip", "nvfp4_device.h"),
+        "source_hash": src_hash("gemm.hip", "nvfp4_device.h", "internal.h"),
         "fetch_scale": round(fs, 4),
         "write_scale": round(ws, 4),
         "per_shape_bytes": shapes,
@@ -921,7 +935,7 @@ def summarize_traffic(fetch_dir, write_dir):
             prod_entry["swiglu"] = {"fetch": int(fm), "write": int(wm)}
     if prod_entry:
         data["producer_single_launch"] = {
-            "source_hash": src_hash("producer.hip", "nvfp4_device.h"), "per_launch_bytes": prod_entry,
+            "source_hash": src_hash("producer.hip", "nvfp4_device.h", "internal.h"), "per_launch_bytes": prod_entry,
             "note": "FETCH_SIZE / WRITE_SIZE of the step's single-launch producers, scaled like the GEMM's"}
         with open(path, "w") as fh:
             json.dump(data, fh, indent=1)

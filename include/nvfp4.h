@@ -242,9 +242,9 @@ nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int
  * accumulated in binary32 in an order of the kernel's choosing.
  * Requirements: K % 64 == 0, N % 16 == 0, ldo >= N, ldo % 4 == 0,
  * M_pad >= M, qa/qw 16-byte aligned, sfa/sfw 4-byte aligned, out 8-byte
- * aligned; N * K/2 <= 2^32 (the packed weight within 4 GiB), K <= 2^25,
+ * aligned; N * K/2 < 2^32 (the packed weight under 4 GiB), K <= 2^25,
  * M_pad < 2^31.  The activation may exceed 4 GiB: the rows are then computed
- * in chunks of floor(2^32 / (K/2)) rounded down to a multiple of 256, one
+ * in chunks of floor((2^32 - 1) / (K/2)) rounded down to a multiple of 256, one
  * launch sequence per chunk in stream order. */
 nvfp4_status nvfp4_gemm(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
                         int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale,

@@ -318,10 +318,11 @@ nvfp4_status nvfp4_swiglu_quantize(const uint16_t* gate, const uint16_t* up, int
     return hip_status(launch_swiglu_pack(gate, up, g2, tensor_scale, qdata, sfa, false, s));
 }
 
-// Activation rows per launch: every byte offset into qa stays below 2^32
-// (the kernel's offsets are 32-bit), in whole 256-row tiles; 0 when K is too
-// wide for even one tile (K > 2^25).
-static int64_t gemm_chunk_rows(int64_t K) { return (((int64_t)1 << 32) / (K / 2)) / 256 * 256; }
+// Activation rows per launch: the chunk's packed rows stay below 2^32 bytes
+// (the kernel's offsets are 32-bit and its loads are range-checked against
+// 2^32 - 1), in whole 256-row tiles; 0 when K is too wide for even one tile
+// (K > 2^25).
+static int64_t gemm_chunk_rows(int64_t K) { return ((((int64_t)1 << 32) - 1) / (K / 2)) / 256 * 256; }
 
 static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,
                               int64_t M_pad, const uint8_t* qw, const uint8_t* sfw, const float* w_scale, int64_t N,
@@ -331,7 +332,7 @@ static nvfp4_status gemm_args(const uint8_t* qa, const uint8_t* sfa, const float
     if (K % 64 != 0 || N % 16 != 0) return NVFP4_ERR_SHAPE;
     // 32-bit byte offsets inside the kernel: the weight must fit them; the
     // activation is launched in row chunks that do (run_gemm)
-    if (N * (K / 2) > ((int64_t)1 << 32) || gemm_chunk_rows(K) == 0) return NVFP4_ERR_SHAPE;
+    if (N * (K / 2) >= ((int64_t)1 << 32) || gemm_chunk_rows(K) == 0) return NVFP4_ERR_SHAPE;
     if (M_pad >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
     if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(sfa, 4) || !aligned(sfw, 4) || !aligned(out, 8) ||
         ldo % 4 != 0 || !aligned(a_scale, 4) || !aligned(w_scale, 4))

@@ -63,6 +63,7 @@ def test_gemm_argument_errors(pkg):
     assert g(P, P, P, 0, 64, P, P, P, 64, 64, P, 64, None) == 1
     assert g(P, P, P, 10, 64, P, P, P, 64, 48, P, 64, None) == 2       # K % 64
     assert g(P, P, P, 10, 64, P, P, P, 1 << 20, 1 << 14, P, 1 << 20, None) == 2   # weight past 4 GiB
+    assert g(P, P, P, 10, 64, P, P, P, 1 << 18, 1 << 15, P, 1 << 18, None) == 2   # weight of exactly 4 GiB
     assert g(P, P, P, 10, 64, P, P, P, 16, 1 << 26, P, 16, None) == 2  # K > 2^25
     assert g(P, P, P, 10, 64, P, P, P, 40, 64, P, 64, None) == 2       # N % 16
     assert g(P, P, P, 10, 8, P, P, P, 64, 64, P, 64, None) == 1        # M_pad < M

@@ -11,8 +11,10 @@
 // as bf16 on gfx950) with exact operands; only the fp32 accumulation order
 // differs from an exact dot product.  A nibble pair decodes with one
 // v_cvt_scalef32_pk_f16_fp4 (scale 256, a power of two, which the
-// instruction applies exactly) followed by one v_pk_mul_f16 by the raw E4M3
-// bits reinterpreted as fp16 (equal to sf * 2^-8, subnormals included).
+// instruction applies exactly) followed by one v_pk_mul_f16 by the block
+// scale as fp16 times 2^-8; v_cvt_scalef32_pk_f16_fp8 converts two scale
+// bytes to those fp16 values at once, exactly, subnormals included, with the
+// sign bit and the NaN code read as E4M3FN defines them.
 //
 // Tiling.  A workgroup of 8 waves (two per SIMD) computes a 256x256 output
 // tile; each wave a 128(M) x 64(N) sub-tile as 4x2 v_mfma_f32_32x32x16_f16
@@ -57,14 +59,16 @@ constexpr int kBM = 256, kBN = 256, kBK = 64, kWM = 128, kWN = 64;
 // Workgroup slots of one wave over the chip (256 CUs, one 512-thread workgroup each).
 constexpr int kWaveSlots = 256;
 
-// Raw E4M3 bits of byte `b` of a scale word, as two fp16 equal to sf * 2^-8.
-__device__ __forceinline__ uint32_t sf_raw2(uint32_t word, int b) {
-    return ((word >> (8 * b)) & 0x7Fu) * 0x00800080u;
+// The E4M3 scales in bytes hb and hb+1 of a scale word, as two fp16 equal to
+// sf * 2^-8 (v_cvt_scalef32_pk_f16_fp8: an exact conversion, subnormals
+// included, with the power-of-two scale applied exactly).
+__device__ __forceinline__ f16x2 sf_pair(uint32_t word, int hb) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word >> (8 * hb), 0x1p-8f, false);
 }
 
-// 8 nibbles (element 2i in the low nibble of byte i) times the block scale.
-__device__ __forceinline__ f16x8 decode8(uint32_t w, uint32_t sraw2) {
-    const f16x2 s = __builtin_bit_cast(f16x2, sraw2);
+// 8 nibbles (element 2i in the low nibble of byte i) times the block scale
+// s (the same fp16 in both halves).
+__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 s) {
     const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s;
     const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s;
     const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s;
@@ -136,13 +140,12 @@ __device__ __forceinline__ ScaleGrp load_grp(__amdgpu_buffer_rsrc_t sf, uint32_t
 }
 
 // Decode part p (row p>>1, words 2(p&1) and 2(p&1)+1: the 16 values of one
-// block) of the thread's staged half rows into LDS: two 16-byte stores.  sc[i]
-// is row i's scale word of the step; hb = 2h indexes the first scale byte of
-// this thread's half row.
-__device__ __forceinline__ void store_part(const RowPack& r, const uint32_t (&sc)[2], int p, _Float16* dst0,
-                                           _Float16* dst1, int hb) {
+// block) of the thread's staged half rows into LDS: two 16-byte stores.  sp[i]
+// holds row i's two block scales of the step for this thread's half row.
+__device__ __forceinline__ void store_part(const RowPack& r, const f16x2 (&sp)[2], int p, _Float16* dst0,
+                                           _Float16* dst1) {
     const int i = p >> 1, wp = p & 1;
-    const uint32_t s2 = sf_raw2(sc[i], hb + wp);
+    const f16x2 s2 = {sp[i][wp], sp[i][wp]};
     _Float16* dst = i == 0 ? dst0 : dst1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -179,7 +182,7 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
     _Float16* dst0 = lds + (st.dop + (CUR ^ 1)) * kTileHalves + st.d0;
     _Float16* dst1 = lds + (st.dop + (CUR ^ 1)) * kTileHalves + st.d1;
     const ScaleGrp& gs = SW < 4 ? gc : gn;
-    const uint32_t sc[2] = {word_of(gs.s[0], SW & 3), word_of(gs.s[1], SW & 3)};
+    const f16x2 sp[2] = {sf_pair(word_of(gs.s[0], SW & 3), st.hb), sf_pair(word_of(gs.s[1], SW & 3), st.hb)};
     const RowPack na = load_row(st.qr, 32u * next_stage, st.q0, st.q1);
     if (LOADG) gn = load_grp<SC4>(st.sr, st.s0, st.s1, next_grp, nit);
     f16x8 wf[2][2], af[2][4];
@@ -199,7 +202,7 @@ __device__ __forceinline__ void k_step(_Float16* __restrict__ lds, f32x16 (&acc)
             for (int i = 0; i < 4; ++i)
                 af[b ^ 1][i] = *reinterpret_cast<const f16x8*>(cA + (arow0 + 32 * i) * kLDK + kk);
         }
-        store_part(ra, sc, j, dst0, dst1, st.hb);
+        store_part(ra, sp, j, dst0, dst1);
         // Four MFMAs in a row share one weight fragment, and the activation
         // fragments run 0..3 then 3..0, so that consecutive instructions
         // change as few operands as possible: under the power limit fewer
@@ -345,10 +348,10 @@ gemm_kernel(GemmArgs a, GemmPart p) {
     RowPack ra = load_row(st.qr, 0u, st.q0, st.q1);
     ScaleGrp gc = load_grp<SC4>(st.sr, st.s0, st.s1, 0, nit), gn = gc;
     {
-        const uint32_t sc[2] = {gc.s[0].x, gc.s[1].x};
+        const f16x2 sp[2] = {sf_pair(gc.s[0].x, st.hb), sf_pair(gc.s[1].x, st.hb)};
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            store_part(ra, sc, p, lds + st.dop * kTileHalves + st.d0, lds + st.dop * kTileHalves + st.d1, st.hb);
+            store_part(ra, sp, p, lds + st.dop * kTileHalves + st.d0, lds + st.dop * kTileHalves + st.d1);
     }
     {
         const uint32_t s1 = nit > 1 ? 1 : 0;

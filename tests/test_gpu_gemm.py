@@ -144,6 +144,31 @@ def test_zero_activation_gives_zero(m):
     assert (out_f64(out) == 0).all()
 
 
+def test_signed_and_nan_scale_bytes_decode_as_the_oracle(m):
+    """Scale bytes the producer never writes, read as E4M3FN like the oracle
+    reads them: the sign bit gives a negative scale and 0x7F (the NaN code)
+    makes every product with its block NaN, so one NaN activation scale turns
+    its output row into NaN and one NaN weight scale its output column."""
+    rng = np.random.default_rng(31)
+    M, N, K = 96, 48, 256
+    a = bf16_np(rng.standard_normal((M, K)))
+    w = bf16_np(0.05 * rng.standard_normal((N, K)))
+    sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, oracle.padded_rows(M))
+    sfa, sfw = sfa.copy(), sfw.copy()
+    sfa[rng.random(sfa.shape) < 0.3] |= 0x80
+    sfw[rng.random(sfw.shape) < 0.3] |= 0x80
+    sfa[5, 3] = 0x7F
+    sfw[7, 0] = 0x7F
+    ref = _par.gemm_rows(qa, sfa, sa, qw, sfw, sw, np.arange(M))
+    nan = np.isnan(ref)
+    assert nan[5].all() and nan[:, 7].all() and nan.sum() == M + N - 1
+    ref_u = _par.gemm_rows(qa, sfa & 0x7F, sa, qw, sfw & 0x7F, sw, np.arange(M))
+    assert not np.allclose(ref[~nan], ref_u[~nan])  # the sign bits change the sums
+    out = out_f64(gpu_gemm(m, sa, qa, sfa, sw, qw, sfw, M))
+    assert np.array_equal(np.isnan(out), nan)
+    check(ref[~nan], out[~nan], "signed scale bytes")
+
+
 def test_extreme_scales_fp16_range(m):
     """Largest and smallest decoded magnitudes (6*448 and 0.5*2^-9) on both
     operands stay exact through the fp16 decode."""

@@ -306,8 +306,13 @@ def main():
     def swiglu_bytes(F):  # two reads of gate+up + QDATA + SFA
         return 2 * M * 2 * F * 2 + M_pad * (F // 2 + F // 16)
 
+    def one_read_bytes(in_cols, K):  # the input read once + QDATA + SFA: what any producer must move
+        return M * in_cols * 2 + M_pad * (K // 2 + K // 16)
+
     flops = {w.name: 2.0 * M * w.N * w.K for w in (wq, wf1, wf2)}
     prod_bytes = {"qkv": mod_bytes(wq.K), "fc1": mod_bytes(wf1.K), "fc2": swiglu_bytes(F)}
+    prod_one_read = {"qkv": one_read_bytes(wq.K, wq.K), "fc1": one_read_bytes(wf1.K, wf1.K),
+                     "fc2": one_read_bytes(2 * F, F)}
     total_flops = sum(flops.values())
     gemm_ms = {nme: med[f"{nme}.gemm"] for nme in flops}
     def prod_parts(nme):
@@ -361,7 +366,9 @@ def main():
                                       "included); GBps and frac_hbm divide these by the time",
                   "counter_bytes": producer_counter_bytes("swiglu" if nme == "fc2" else "modulate"),
                   "GBps": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9, 1),
-                  "frac_hbm": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                  "frac_hbm": round(prod_bytes[nme] / (prod_ms[nme] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "one_read_bytes": prod_one_read[nme],
+                  "frac_hbm_one_read": round(prod_one_read[nme] / (prod_ms[nme] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             for nme in flops
         },
         "gemm": {

@@ -945,8 +945,9 @@ __device__ __forceinline__ uint4 ld16o(const char* base, uint32_t off) {
 // plus a wave-uniform scalar offset (local group t times the grid stride in
 // bytes), so that stepping from one row group to the next takes no VALU
 // address arithmetic (a 64-bit multiply-add per access before; measured 1-2%
-// faster per launch).  The same change made the SwiGLU single launch 0.8%
-// slower, and it keeps its pointer accesses.  Every offset the kernel forms is
+// faster per launch).  In the SwiGLU single launch the same change measured
+// slower in pass 2 and no different in pass 1, and it keeps its pointer
+// accesses.  Every offset the kernel forms is
 // below 2^32 (checked by the caller), within the descriptors' range of
 // 2^32 - 1 bytes.
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));

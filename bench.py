@@ -93,6 +93,29 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
+def modulation_bytes(M: int, M_pad: int, K: int) -> int:
+    """Algorithmic bytes of the modulation producer: two reads of x [M, K] bf16,
+    QDATA [M_pad, K/2] and SFA [M_pad, K/16] written (padding rows included)."""
+    return 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
+
+
+def swiglu_bytes(M: int, M_pad: int, F: int) -> int:
+    """Algorithmic bytes of the SwiGLU producer: two reads of gate/up [M, 2F]
+    bf16, QDATA and SFA of h [M_pad, F] written."""
+    return 2 * M * 2 * F * 2 + M_pad * (F // 2 + F // 16)
+
+
+def one_read_bytes(M: int, M_pad: int, in_cols: int, K: int) -> int:
+    """What any producer must move: the bf16 input [M, in_cols] read once,
+    QDATA and SFA of [M_pad, K] written."""
+    return M * in_cols * 2 + M_pad * (K // 2 + K // 16)
+
+
+def gemm_flop(M: int, N: int, K: int) -> float:
+    """Algorithmic flops of the [M, K] x [N, K]^T product over the logical rows."""
+    return 2.0 * M * N * K
+
+
 def traffic_entry(kernel: str, source_hash: str):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain-copy calibration), if they were taken on the
@@ -300,19 +323,11 @@ def main():
     standalone = {} if args.no_standalone else standalone_producers(seq, stream, dev, reps=20)
 
     # algorithmic work
-    def mod_bytes(K):  # two reads of x + QDATA + SFA written (padded rows included)
-        return 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
-
-    def swiglu_bytes(F):  # two reads of gate+up + QDATA + SFA
-        return 2 * M * 2 * F * 2 + M_pad * (F // 2 + F // 16)
-
-    def one_read_bytes(in_cols, K):  # the input read once + QDATA + SFA: what any producer must move
-        return M * in_cols * 2 + M_pad * (K // 2 + K // 16)
-
-    flops = {w.name: 2.0 * M * w.N * w.K for w in (wq, wf1, wf2)}
-    prod_bytes = {"qkv": mod_bytes(wq.K), "fc1": mod_bytes(wf1.K), "fc2": swiglu_bytes(F)}
-    prod_one_read = {"qkv": one_read_bytes(wq.K, wq.K), "fc1": one_read_bytes(wf1.K, wf1.K),
-                     "fc2": one_read_bytes(2 * F, F)}
+    flops = {w.name: gemm_flop(M, w.N, w.K) for w in (wq, wf1, wf2)}
+    prod_bytes = {"qkv": modulation_bytes(M, M_pad, wq.K), "fc1": modulation_bytes(M, M_pad, wf1.K),
+                  "fc2": swiglu_bytes(M, M_pad, F)}
+    prod_one_read = {"qkv": one_read_bytes(M, M_pad, wq.K, wq.K), "fc1": one_read_bytes(M, M_pad, wf1.K, wf1.K),
+                     "fc2": one_read_bytes(M, M_pad, 2 * F, F)}
     total_flops = sum(flops.values())
     gemm_ms = {nme: med[f"{nme}.gemm"] for nme in flops}
     def prod_parts(nme):
@@ -645,7 +660,7 @@ def cpu_baseline(args, x_h, segs, gu_h, works):
     M, M_pad, K = wq.M, wq.m_pad, wq.K
     rs, sh, sc = wq.segments()
     seg = oracle.Segments(rs, sh, sc)
-    mod_bytes = 2 * M * K * 2 + M_pad * (K // 2 + K // 16)
+    mod_bytes = modulation_bytes(M, M_pad, K)
 
     t0 = time.perf_counter()
     _oracle_modulation_producer(oracle, x_h, seg, M, M_pad, None, 1)

@@ -263,7 +263,9 @@ size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * sums land in the workspace, then added in K order and scaled by alpha.  The
  * result satisfies the same contract as nvfp4_gemm (only the binary32
  * summation order differs).  The workspace holds no state between calls;
- * calls sharing it must not overlap.  Same requirements and errors as
+ * calls sharing it must not overlap.  Like nvfp4_gemm it enqueues kernels
+ * only (no memset, no allocation), so a call can be captured into a HIP graph
+ * and replayed with new operands in the same buffers.  Same requirements and errors as
  * nvfp4_gemm, plus NVFP4_ERR_INVALID_ARGUMENT for a missing or short
  * workspace. */
 nvfp4_status nvfp4_gemm_ws(const uint8_t* qa, const uint8_t* sfa, const float* a_scale, int64_t M,

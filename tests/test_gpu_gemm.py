@@ -590,3 +590,58 @@ def test_activation_past_4_gib_runs_in_row_chunks(m):
     want = oracle.gate_residual_rows(o, seg_rs, gate, rblock[rows % P])
     got = host_u16(res[ridx])
     assert np.array_equal(got, want), first_mismatch(got, want)
+
+
+def test_gemm_ws_under_graph_capture_replays_match_eager(m):
+    """nvfp4_gemm_ws captured into a HIP graph on a shape whose last wave of
+    tiles is split along K (256 whole tiles and 4 split ones, then the
+    finalize launch): four replays with new operands copied into the captured
+    buffers, each bit for bit equal to the same call run eagerly in between.
+    The library enqueues kernels only (no memset), so the graph holds kernels
+    only."""
+    dev = device()
+    M, N, K = 13 * 256, 20 * 256, 1024
+    m_pad = oracle.padded_rows(M)
+    nbytes = int(m.nvfp4_gemm_workspace_bytes(M, N, K))
+    assert nbytes > 0
+    bufs = {}
+
+    def load(seed):
+        rng = np.random.default_rng(seed)
+        a = bf16_np(rng.standard_normal((M, K)))
+        w = bf16_np(0.05 * rng.standard_normal((N, K)))
+        sa, qa, sfa, sw, qw, sfw = oracle_quantized(a, w, m_pad)
+        vals = dict(qa=qa, sfa=sfa, qw=qw, sfw=sfw, sa=np.array([sa], np.float32), sw=np.array([sw], np.float32))
+        for k, v in vals.items():
+            t = torch.from_numpy(np.ascontiguousarray(v))
+            if k in bufs:
+                bufs[k].copy_(t)
+            else:
+                bufs[k] = t.to(dev)
+
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_eager = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def call(o, wsp):
+        b = bufs
+        m.nvfp4_gemm_ws(b["qa"], b["sfa"], b["sa"], M, m_pad, b["qw"], b["sfw"], b["sw"], N, K, o, N, wsp, nbytes)
+
+    load(200)
+    call(out, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):  # captured on the graph's own stream, the current one inside
+        call(out, ws)
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((201, 202, 203, 204)):
+        print(f"replay {rep} with operand seed {seed}", flush=True)
+        load(seed)
+        torch.cuda.synchronize()
+        call(ref, ws_eager)  # eager work between the replays
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep

@@ -166,8 +166,14 @@ nvfp4_status nvfp4_modulate_pack(const uint16_t* x, int64_t M, int64_t D, int64_
  * amax, scale code 0x7F and zero codes in every block, for that call only,
  * and adds one to the workspace's timeout count
  * (NVFP4_WORKSPACE_TIMEOUT_COUNT_OFFSET).
- * Calls that can overlap in time must use different workspaces.  When
- * D > 16384, or x spans 4 GiB or more, it enqueues the two passes instead.
+ * Calls that can overlap in time must use different workspaces.  Each call
+ * takes its barrier tag from the host when it is enqueued, so a call captured
+ * into a HIP graph would replay one tag and find the previous replay's words
+ * already arrived: under graph capture use nvfp4_modulate_quantize_noalloc
+ * (its words are cleared by a kernel on every call) or the two calls
+ * nvfp4_modulate_absmax + nvfp4_modulate_pack (whose words return to zero).
+ * When D > 16384, or x spans 4 GiB or more, it enqueues the two passes
+ * instead.
  * Same requirements as nvfp4_modulate_absmax and nvfp4_modulate_pack
  * together. */
 nvfp4_status nvfp4_modulate_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx,
@@ -195,8 +201,8 @@ nvfp4_status nvfp4_modulate_quantize_noalloc(const uint16_t* x, int64_t M, int64
 /* The plain quantizer: nvfp4_modulate_quantize with y = x (no modulation), for
  * activations that need none (the attention-output projection's input,
  * "NVFP4 Streaming Design", P0/P2: the widths 5376, 7168, 14336) and for
- * prepacking weights.  Same launch structure, outputs, workspace and
- * requirements, without the segment table. */
+ * prepacking weights.  Same launch structure, outputs, workspace,
+ * requirements and graph-capture caveat, without the segment table. */
 nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t M, int64_t D, int64_t ldx, void* workspace,
                             float* tensor_scale, float* amax_out, uint8_t* qdata, uint8_t* sfa, int64_t M_pad,
                             void* stream);
@@ -223,7 +229,8 @@ nvfp4_status nvfp4_swiglu_pack(const uint16_t* gate, const uint16_t* up, int64_t
  * followed by nvfp4_swiglu_pack, byte for byte): after the silu table fill,
  * one launch runs pass 1, a grid barrier and pass 2, keeping h of the rows
  * each workgroup visited last in registers, as nvfp4_modulate_quantize does
- * (same workspace, the same barrier with helping, the same bound).  When
+ * (same workspace, the same barrier with helping, the same bound, and the
+ * same caveat under graph capture: use the two calls there).  When
  * F > 16384, or gate/up spans
  * 4 GiB or more, it enqueues the two passes instead.  Same arguments,
  * requirements and errors as the two calls together. */

@@ -146,6 +146,12 @@ def _torch_stream(stream, dev: torch.device):
     return torch.cuda.ExternalStream(int(stream), device=dev)
 
 
+def _capturing(st) -> bool:
+    """Whether work enqueued on torch stream st is being captured into a graph."""
+    with torch.cuda.stream(st):
+        return torch.cuda.is_current_stream_capturing()
+
+
 def workspace(device=None, stream=None) -> torch.Tensor:
     """The producers' workspace for one (device, stream) pair, zero-filled on
     that stream when first made.  Calls on one stream run in order and may
@@ -328,7 +334,10 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
     """x [M, D] bf16 -> (qdata [M_pad, D/2] u8, sfa [M_pad, D/16] u8, tensor_scale f32[1], amax f32[1]).
 
     single_pass: one nvfp4_modulate_quantize launch; else nvfp4_modulate_absmax
-    then nvfp4_modulate_pack (identical bytes)."""
+    then nvfp4_modulate_pack (identical bytes).  Under graph capture the two
+    launches are used either way: the single launch's barrier tag comes from
+    the host when it is enqueued, so a replay would meet the previous replay's
+    words, while the two-pass words return to zero after every call."""
     _bits16(x)
     M, D = x.shape
     if x.stride(1) != 1:
@@ -342,7 +351,7 @@ def modulate_quantize(x: torch.Tensor, row_start, shift: torch.Tensor, scale: to
         amax = torch.empty(1, dtype=torch.float32, device=dev)
         q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
-    if single_pass:
+    if single_pass and not _capturing(st):
         nvfp4_modulate_quantize(x, M, D, x.stride(0), seg, workspace(dev, st), ts, amax, q, s, m_pad, st)
     else:
         nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev, st), ts, amax, st)
@@ -355,7 +364,8 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, com
     """gate/up [M, 2F] bf16 (gate = first F columns) -> (qdata, sfa, tensor_scale, amax).
 
     combined: one nvfp4_swiglu_quantize call; else nvfp4_swiglu_absmax then
-    nvfp4_swiglu_pack (identical bytes)."""
+    nvfp4_swiglu_pack (identical bytes); the latter under graph capture, as in
+    modulate_quantize."""
     _bits16(gu)
     M, F2 = gu.shape
     F = F2 // 2
@@ -370,7 +380,7 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, com
         q = torch.empty((m_pad, F // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((m_pad, F // 16), dtype=torch.uint8, device=dev)
     up = gu.data_ptr() + F * gu.element_size()
-    if combined:
+    if combined and not _capturing(st):
         nvfp4_swiglu_quantize(gu, up, M, F, gu.stride(0), workspace(dev, st), ts, amax, q, s, m_pad, st)
     else:
         nvfp4_swiglu_absmax(gu, up, M, F, gu.stride(0), workspace(dev, st), ts, amax, st)
@@ -378,8 +388,27 @@ def swiglu_quantize(gu: torch.Tensor, m_pad: int | None = None, stream=None, com
     return q, s, ts, amax
 
 
+_identity: dict[tuple[int, int], tuple[torch.Tensor, torch.Tensor]] = {}
+
+
+def _identity_modulation(dev: torch.device, D: int, st):
+    """shift = -0 and scale = +0 rows of width D (y = bf16(bf16(x * 1) + -0) = x
+    for every bf16 x), kept for the life of the process: a graph that captured
+    a call reads them on every replay."""
+    key = (dev.index, D)
+    if key not in _identity:
+        with torch.cuda.stream(st):
+            _identity[key] = (torch.full((1, D), -0.0, dtype=torch.bfloat16, device=dev),
+                              torch.zeros((1, D), dtype=torch.bfloat16, device=dev))
+    return _identity[key]
+
+
 def quantize(x: torch.Tensor, m_pad: int | None = None, stream=None):
-    """Plain quantizer: x [M, D] bf16 -> (qdata [M_pad, D/2], sfa [M_pad, D/16], tensor_scale f32[1], amax f32[1])."""
+    """Plain quantizer: x [M, D] bf16 -> (qdata [M_pad, D/2], sfa [M_pad, D/16], tensor_scale f32[1], amax f32[1]).
+
+    Under graph capture (see modulate_quantize) it runs the two modulation
+    passes with the identity modulation, scale +0 and shift -0, which leaves
+    every bf16 value as it is: the same bytes."""
     _bits16(x)
     M, D = x.shape
     if x.stride(1) != 1:
@@ -392,7 +421,14 @@ def quantize(x: torch.Tensor, m_pad: int | None = None, stream=None):
         amax = torch.empty(1, dtype=torch.float32, device=dev)
         q = torch.empty((m_pad, D // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((m_pad, D // 16), dtype=torch.uint8, device=dev)
-    nvfp4_quantize(x, M, D, x.stride(0), workspace(dev, st), ts, amax, q, s, m_pad, st)
+    if _capturing(st):
+        shift0, scale0 = _identity_modulation(dev, D, st)
+        seg, keep = make_segments([0, M], shift0, scale0)
+        nvfp4_modulate_absmax(x, M, D, x.stride(0), seg, workspace(dev, st), ts, amax, st)
+        nvfp4_modulate_pack(x, M, D, x.stride(0), seg, ts, q, s, m_pad, st)
+        del keep
+    else:
+        nvfp4_quantize(x, M, D, x.stride(0), workspace(dev, st), ts, amax, q, s, m_pad, st)
     return q, s, ts, amax
 
 

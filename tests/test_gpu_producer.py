@@ -718,3 +718,51 @@ def test_swiglu_input_past_4_gib(m):
     assert np.array_equal(gs, os_), first_mismatch(gs, os_)
     assert np.array_equal(gq, oq), first_mismatch(gq, oq)
     assert not host(q[M:]).any() and not host(s[M:]).any()
+
+
+def test_conveniences_under_graph_capture_replay_like_eager(m):
+    """modulate_quantize, swiglu_quantize and quantize with their defaults,
+    captured into a HIP graph, take their two-launch forms (the single
+    launch's barrier tag comes from the host and would replay): four replays
+    with new inputs copied into the captured input buffers, each byte-equal
+    to the same conveniences run eagerly (single launches) in between."""
+    dev = device()
+    M, D, F = 3000, 2048, 1024
+    rs = [0, 1700, M]
+    sh = to_dev_u16(synth.normal_bf16(61, 1, (2, D), 0.1))
+    sc = to_dev_u16(synth.normal_bf16(61, 2, (2, D), 0.1))
+    x = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+
+    def fill(seed):
+        x.copy_(to_dev_u16(synth.add_outliers_t3(synth.normal_bf16(seed, 0, (M, D), 1.0), seed, 0.001, 20.0)))
+        gu.copy_(to_dev_u16(synth.normal_bf16(seed, 3, (M, 2 * F), 1.0)))
+
+    def run_all():
+        return (m.modulate_quantize(x, rs, sh, sc), m.swiglu_quantize(gu), m.quantize(x))
+
+    def bytes_of(res):
+        return [tuple(host(t).tobytes() for t in r) for r in res]
+
+    fill(300)
+    run_all()  # eager first: workspaces of this stream and the library's tables
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):  # captured on the graph's own stream, the current one inside
+        captured = run_all()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((301, 302, 303, 304)):
+        print(f"replay {rep} with input seed {seed}", flush=True)
+        fill(seed)
+        torch.cuda.synchronize()
+        want = bytes_of(run_all())  # eager single launches between the replays
+        for r in captured:
+            for t in r:
+                t.fill_(0x5A if t.dtype == torch.uint8 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = bytes_of(captured)
+        for name, gw, ww in zip(("modulation", "swiglu", "plain"), got, want):
+            for part, a, b in zip(("qdata", "sfa", "tensor scale", "amax"), gw, ww):
+                assert a == b, (rep, name, part)

@@ -33,3 +33,15 @@ def test_gemm_flops():
     assert bench.gemm_flop(M, 21504, 5376) == 8_742_088_212_480
     assert bench.gemm_flop(M, 14336, 5376) == 5_828_058_808_320
     assert bench.gemm_flop(M, 5376, 14336) == 5_828_058_808_320
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    """Counter readings are kept while the kernels' code is unchanged: comment
+    and whitespace edits keep the normalized text, code edits change it, and
+    comment markers inside string literals are code."""
+    base = 'int f(int a) { // doubles a\n  return a * 2; /* note */ }\nconst char* s = "x // y";\n'
+    same = '/* header */\nint f(int a)\n{\n    return a * 2;   // twice\n}\nconst char* s = "x // y";'
+    assert bench.code_only(base) == bench.code_only(same)
+    assert bench.code_only(base) != bench.code_only(base.replace("a * 2", "a * 3"))
+    assert bench.code_only(base) != bench.code_only(base.replace('"x // y"', '"x /* y"'))
+    assert "y" in bench.code_only(base) and "doubles" not in bench.code_only(base)
